@@ -1,0 +1,187 @@
+"""CPU FP64 oracle for RMSNorm forward / backward and the fused
+add-RMSNorm-FP8 1x128 block-quant producer.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package.  The arithmetic is
+in ``oracle.c`` (plain sequential C, FP64, no fast-math); this module only
+compiles it with gcc and marshals numpy arrays through ctypes.
+
+Parity status of each function (what pins it, independently of itself) is
+stated in the test files ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fno-fast-math",
+               "-ffp-contract=off", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    vp = ctypes.c_void_p
+    lib.rno_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.rno_bf16_to_double.restype = ctypes.c_double
+    lib.rno_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.rno_double_to_bf16.restype = ctypes.c_uint16
+    lib.rno_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.rno_e4m3_to_double.restype = ctypes.c_double
+    lib.rno_float_to_e4m3.argtypes = [ctypes.c_float]
+    lib.rno_float_to_e4m3.restype = ctypes.c_uint8
+    lib.rno_rmsnorm_fwd.argtypes = [vp, i64, i32, vp, i32, i64, i64, f32, vp, i64, vp]
+    lib.rno_rmsnorm_fwd.restype = i32
+    lib.rno_rmsnorm_bwd.argtypes = [vp, i64, vp, i64, i32, vp, i32, vp, i64, i64, vp, i64, vp]
+    lib.rno_rmsnorm_bwd.restype = i32
+    lib.rno_block_quant_e4m3.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64]
+    lib.rno_block_quant_e4m3.restype = i32
+    lib.rno_add_rmsnorm_fp8.argtypes = [vp, i64, vp, i64, vp, i64, i64, f32,
+                                        vp, i64, vp, vp, i64, vp, i64, vp, i64, vp, i64]
+    lib.rno_add_rmsnorm_fp8.restype = i32
+    _lib = lib
+    return lib
+
+
+# --------------------------------------------------------------------------
+# helpers: arrays are numpy; bf16 tensors travel as uint16 bit patterns
+# --------------------------------------------------------------------------
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 arrays or uint16 bf16 bit patterns, got %s" % a.dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _row_stride(a: np.ndarray) -> int:
+    assert a.ndim == 2 and a.strides[1] == a.itemsize, "rows must be contiguous"
+    return a.strides[0] // a.itemsize
+
+
+def bf16_to_double(b: int) -> float:
+    return _load().rno_bf16_to_double(int(b))
+
+
+def double_to_bf16(v: float) -> int:
+    return int(_load().rno_double_to_bf16(float(v)))
+
+
+def e4m3_to_double(c: int) -> float:
+    return _load().rno_e4m3_to_double(int(c))
+
+
+def float_to_e4m3(v) -> int:
+    return int(_load().rno_float_to_e4m3(float(np.float32(v))))
+
+
+def bf16_decode_array(a: np.ndarray) -> np.ndarray:
+    """Vectorised exact decode of bf16 bit patterns (uint16) to float64."""
+    lib = _load()
+    flat = np.ascontiguousarray(a).ravel()
+    out = np.fromiter((lib.rno_bf16_to_double(int(v)) for v in flat), dtype=np.float64, count=flat.size)
+    return out.reshape(a.shape)
+
+
+def rmsnorm_fwd(x: np.ndarray, w: np.ndarray, eps: float, want_y: bool = True):
+    """FP64 forward: returns (y unrounded [T,H] float64 or None, rstd [T] float64)."""
+    lib = _load()
+    T, H = x.shape
+    y = np.empty((T, H), dtype=np.float64) if want_y else None
+    rstd = np.empty((T,), dtype=np.float64)
+    rc = lib.rno_rmsnorm_fwd(_ptr(x), _row_stride(x) if T else H, _dtype_code(x),
+                             _ptr(w), _dtype_code(w), T, H, np.float32(eps),
+                             _ptr(y), H, _ptr(rstd))
+    if rc:
+        raise ValueError("oracle rmsnorm_fwd rejected the arguments (%d)" % rc)
+    return y, rstd
+
+
+def rmsnorm_bwd(dy: np.ndarray, x: np.ndarray, w: np.ndarray, rstd: np.ndarray,
+                want_dx: bool = True, want_dw: bool = True):
+    """FP64 backward at the given rstd: returns (dx [T,H] float64 or None, dw [H] float64 or None)."""
+    lib = _load()
+    assert dy.dtype == x.dtype and dy.shape == x.shape
+    T, H = x.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+    dx = np.empty((T, H), dtype=np.float64) if want_dx else None
+    dw = np.empty((H,), dtype=np.float64) if want_dw else None
+    rc = lib.rno_rmsnorm_bwd(_ptr(dy), _row_stride(dy) if T else H, _ptr(x), _row_stride(x) if T else H,
+                             _dtype_code(x), _ptr(w), _dtype_code(w), _ptr(rstd), T, H,
+                             _ptr(dx), H, _ptr(dw))
+    if rc:
+        raise ValueError("oracle rmsnorm_bwd rejected the arguments (%d)" % rc)
+    return dx, dw
+
+
+def block_quant_e4m3(normed_bf16: np.ndarray, scale_ld: int | None = None):
+    """Quantise bf16 normed values (uint16 [T,H]) per 1x128 block.
+
+    Returns (scale [H/128, scale_ld] float32 with padding rows left NaN, codes [T,H] uint8)."""
+    lib = _load()
+    T, H = normed_bf16.shape
+    if scale_ld is None:
+        scale_ld = (T + 3) // 4 * 4
+    scale = np.full((H // 128, scale_ld), np.nan, dtype=np.float32)
+    codes = np.empty((T, H), dtype=np.uint8)
+    rc = lib.rno_block_quant_e4m3(_ptr(normed_bf16), _row_stride(normed_bf16) if T else H, T, H,
+                                  _ptr(scale), scale_ld, _ptr(codes), H)
+    if rc:
+        raise ValueError("oracle block_quant_e4m3 rejected the arguments (%d)" % rc)
+    return scale, codes
+
+
+def add_rmsnorm_fp8(x: np.ndarray, res: np.ndarray, w: np.ndarray, eps: float,
+                    scale_ld: int | None = None):
+    """Full FP64 fused producer.
+
+    Returns dict with h (uint16 bf16 [T,H]), rstd (float64 [T]), normed (float64 [T,H],
+    unrounded), normed_bf16 (uint16 [T,H]), scale (float32 [H/128, scale_ld], NaN padding),
+    codes (uint8 [T,H]) -- scale and codes quantised from the oracle's own normed_bf16."""
+    lib = _load()
+    T, H = x.shape
+    if scale_ld is None:
+        scale_ld = (T + 3) // 4 * 4
+    h = np.empty((T, H), dtype=np.uint16)
+    rstd = np.empty((T,), dtype=np.float64)
+    normed = np.empty((T, H), dtype=np.float64)
+    nb = np.empty((T, H), dtype=np.uint16)
+    scale = np.full((H // 128, scale_ld), np.nan, dtype=np.float32)
+    codes = np.empty((T, H), dtype=np.uint8)
+    rc = lib.rno_add_rmsnorm_fp8(_ptr(x), _row_stride(x) if T else H, _ptr(res), _row_stride(res) if T else H,
+                                 _ptr(w), T, H, np.float32(eps),
+                                 _ptr(h), H, _ptr(rstd), _ptr(normed), H, _ptr(nb), H,
+                                 _ptr(scale), scale_ld, _ptr(codes), H)
+    if rc:
+        raise ValueError("oracle add_rmsnorm_fp8 rejected the arguments (%d)" % rc)
+    return dict(h=h, rstd=rstd, normed=normed, normed_bf16=nb, scale=scale, codes=codes)

@@ -1,0 +1,344 @@
+/*
+ * oracle.c -- CPU reference for row-wise RMSNorm forward, its backward (dX and
+ * the weight gradient dW) and the fused residual-add + RMSNorm + FP8 e4m3
+ * 1x128 block-quant producer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent checker of the HIP
+ * library.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline may load it; the product path never calls it and shares no code,
+ * header, table or helper with it.
+ *
+ * Everything is plain, sequential C in FP64 (built without fast-math and with
+ * floating-point contraction off).  Inputs are decoded exactly to double with
+ * this file's own bf16 / fp32 decoders; results that the method defines in FP64
+ * are returned unrounded, so a test can state its tolerance against the exact
+ * value.  The two places where the method itself fixes fp32 arithmetic (the
+ * per-block scale and the quotient that is quantised) are computed in fp32
+ * exactly as the method states them.
+ *
+ * Sources (the method is defined on these pages; no code was taken from them):
+ *  - FlashInfer commit #5741 "cake_rmsnorm_train" (quoted on the FlashInfer
+ *    PR #4480 page), sections Summary, Design (Forward / Backward) and
+ *    Accuracy: y = x*rstd*w with the fp32 reciprocal RMS saved for the
+ *    backward; dx = rstd*(g*w - mean(g*w*xhat)*xhat); dw the column sum of
+ *    g*x*rstd over rows; h_new = bf16(x + residual) is what gets normalised.
+ *  - FlashInfer PR #4480 "Add FusedAddRMSNormFP8BlockQuant", description
+ *    (Kernel, API) and the review thread: residual updated in place with the
+ *    pre-norm sum, bf16 normed output, fp32 scale = amax/448 per 1x128 block
+ *    in the column-major (H/128, round_up(T,4)) layout, e4m3 codes quantised
+ *    from the bf16-rounded normed values.
+ *
+ * Readings taken where the pages are silent (each is also listed in the
+ * design notes of the repository):
+ *  R1  rstd = 1/sqrt(mean(x^2) + eps): eps is added to the mean inside the
+ *      square root; the weight multiplies as plain w (not 1+w).
+ *  R2  eps is the fp32 value passed by the caller, widened exactly to double.
+ *  R3  the backward uses the forward's stored rstd (an input), not a
+ *      recomputation from x.
+ *  R4  the fused producer normalises the bf16-rounded sum h = bf16(x + r).
+ *  R5  scale = fp32(amax) / 448.0f as one IEEE fp32 division (round to
+ *      nearest even); an all-zero block has scale 0 and all codes 0x00.
+ *  R6  code = e4m3fn(fp32(n) / scale): IEEE fp32 division, then round to
+ *      nearest even onto the E4M3FN grid, saturating to +-448, sign kept
+ *      (a negative value that rounds to zero is 0x80).
+ *  R7  scale layout: element (row m, block k) lives at scale[k*scale_ld + m];
+ *      padding rows m in [T, scale_ld) are not written.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <stdint.h>
+#include <string.h>
+
+#define RNO_F32 0
+#define RNO_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* bf16 codec (bf16 = the upper 16 bits of an IEEE binary32).                */
+/* ------------------------------------------------------------------------ */
+
+/* Exact decode: a bf16 pattern is a binary32 whose low 16 bits are zero. */
+double rno_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, in one rounding.
+ * bf16 has 8 significant bits, the binary32 exponent range and subnormals
+ * down to 2^-133.  Values at or beyond the overflow threshold become +-inf
+ * (never produced by the workloads here). */
+uint16_t rno_double_to_bf16(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v);
+    uint16_t sign = neg ? 0x8000 : 0;
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);               /* a = f * 2^e, 0.5 <= f < 1 */
+    int qexp = e - 8;                 /* quantum of an 8-significant-bit value */
+    if (qexp < -133) qexp = -133;     /* bf16 subnormal quantum */
+    double quantum = ldexp(1.0, qexp);
+    double k = a / quantum;           /* exact: division by a power of two */
+    double fl = floor(k);
+    double frac = k - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;          /* exactly representable in bf16 */
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float rf = (float)r;              /* exact: bf16 values are binary32 values */
+    uint32_t u;
+    memcpy(&u, &rf, sizeof u);
+    return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3FN codec: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinity;  */
+/* S.1111.111 is NaN; largest finite 1.75 * 2^8 = 448; subnormals k * 2^-9.  */
+/* ------------------------------------------------------------------------ */
+
+double rno_e4m3_to_double(uint8_t c)
+{
+    int neg = (c >> 7) & 1;
+    int ex = (c >> 3) & 0xF;
+    int m = c & 7;
+    double v;
+    if (ex == 0xF && m == 7) return NAN;
+    if (ex == 0)
+        v = ldexp((double)m, -9);                 /* m/8 * 2^-6 */
+    else
+        v = ldexp(1.0 + m / 8.0, ex - 7);
+    return neg ? -v : v;
+}
+
+/* Encode an exactly representable non-negative E4M3 magnitude into 7 bits. */
+static uint8_t encode_e4m3_magnitude(double r)
+{
+    if (r == 0.0) return 0;
+    if (r < ldexp(1.0, -6))                        /* subnormal: r = m * 2^-9 */
+        return (uint8_t)(r / ldexp(1.0, -9));
+    int e;
+    double f = frexp(r, &e);                       /* r = f * 2^e, f in [0.5,1) */
+    int ex = e - 1 + 7;                            /* r = (2f) * 2^(e-1) */
+    int m = (int)((2.0 * f - 1.0) * 8.0);          /* exact for grid values */
+    return (uint8_t)((ex << 3) | m);
+}
+
+/* Round a binary32 value to E4M3FN, nearest-even, saturating to +-448. */
+uint8_t rno_float_to_e4m3(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int qexp;
+    if (a < ldexp(1.0, -6)) {
+        qexp = -9;                                 /* subnormal spacing */
+    } else {
+        int e;
+        (void)frexp(a, &e);                        /* a in [2^(e-1), 2^e) */
+        qexp = (e - 1) - 3;                        /* 3 mantissa bits */
+    }
+    double quantum = ldexp(1.0, qexp);
+    double k = a / quantum;                        /* exact */
+    double fl = floor(k);
+    double frac = k - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;                       /* may carry into next binade */
+    if (r > 448.0) r = 448.0;
+    return (uint8_t)(sign | encode_e4m3_magnitude(r));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element access.                                                           */
+/* ------------------------------------------------------------------------ */
+
+static double load_elem(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == RNO_BF16) return rno_bf16_to_double(((const uint16_t*)base)[idx]);
+    return (double)((const float*)base)[idx];
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm forward.                                                          */
+/* Cake commit #5741, Design: Forward -- per row an fp32 sum of squares, the */
+/* reciprocal RMS rstd, y = x*rstd*w.  Here every step is FP64 and y is      */
+/* returned unrounded (readings R1, R2).                                     */
+/* ------------------------------------------------------------------------ */
+
+int rno_rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype,
+                    const void* w, int w_dtype,
+                    int64_t T, int64_t H, float eps,
+                    double* y, int64_t ldy,      /* may be NULL */
+                    double* rstd)                /* may be NULL */
+{
+    if (T < 0 || H <= 0) return 1;
+    for (int64_t r = 0; r < T; ++r) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = load_elem(x, x_dtype, r * ldx + j);
+            ss += v * v;
+        }
+        double ms = ss / (double)H;
+        double rs = 1.0 / sqrt(ms + (double)eps);
+        if (rstd) rstd[r] = rs;
+        if (y) {
+            for (int64_t j = 0; j < H; ++j) {
+                double v = load_elem(x, x_dtype, r * ldx + j);
+                y[r * ldy + j] = v * rs * load_elem(w, w_dtype, j);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm backward.                                                         */
+/* Cake commit #5741, Design: Backward -- xhat = x*rstd,                     */
+/* dx = rstd*(g*w - mean_j(g*w*xhat)*xhat); dw_j = sum over rows of          */
+/* g*x*rstd (the eager form quoted in its Accuracy section).  rstd is the    */
+/* forward's stored value, passed in (reading R3).  dW is accumulated over   */
+/* rows 0..T-1 in order, in FP64, and written (not added to) into dw.        */
+/* ------------------------------------------------------------------------ */
+
+int rno_rmsnorm_bwd(const void* dy, int64_t lddy,
+                    const void* x, int64_t ldx, int x_dtype,
+                    const void* w, int w_dtype,
+                    const double* rstd,
+                    int64_t T, int64_t H,
+                    double* dx, int64_t lddx,    /* may be NULL */
+                    double* dw)                  /* may be NULL; H entries */
+{
+    if (T < 0 || H <= 0) return 1;
+    if (dw)
+        for (int64_t j = 0; j < H; ++j) dw[j] = 0.0;
+    for (int64_t r = 0; r < T; ++r) {
+        double rs = rstd[r];
+        if (dx) {
+            double dot = 0.0;                    /* sum_j g*w*xhat */
+            for (int64_t j = 0; j < H; ++j) {
+                double g = load_elem(dy, x_dtype, r * lddy + j);
+                double xv = load_elem(x, x_dtype, r * ldx + j);
+                double wv = load_elem(w, w_dtype, j);
+                dot += g * wv * (xv * rs);
+            }
+            double c = dot / (double)H;
+            for (int64_t j = 0; j < H; ++j) {
+                double g = load_elem(dy, x_dtype, r * lddy + j);
+                double xv = load_elem(x, x_dtype, r * ldx + j);
+                double wv = load_elem(w, w_dtype, j);
+                double xhat = xv * rs;
+                dx[r * lddx + j] = rs * (g * wv - c * xhat);
+            }
+        }
+        if (dw) {
+            for (int64_t j = 0; j < H; ++j) {
+                double g = load_elem(dy, x_dtype, r * lddy + j);
+                double xv = load_elem(x, x_dtype, r * ldx + j);
+                dw[j] += g * xv * rs;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1x128 block quantisation of bf16 normed values to E4M3FN.                 */
+/* FlashInfer PR #4480, description (Kernel) and the review thread:          */
+/* per row and per 128-column block, scale = amax/448 in fp32; the codes are */
+/* the e4m3 rounding of normed/scale; scales stored column-major with the    */
+/* row index fastest (readings R5, R6, R7).                                  */
+/* ------------------------------------------------------------------------ */
+
+int rno_block_quant_e4m3(const uint16_t* normed, int64_t ldn,
+                         int64_t T, int64_t H,
+                         float* scale, int64_t scale_ld,
+                         uint8_t* codes, int64_t ldq)
+{
+    if (T < 0 || H <= 0 || H % 128 != 0 || scale_ld < T) return 1;
+    int64_t nblk = H / 128;
+    for (int64_t r = 0; r < T; ++r) {
+        for (int64_t k = 0; k < nblk; ++k) {
+            float amax = 0.0f;
+            for (int64_t j = 128 * k; j < 128 * k + 128; ++j) {
+                float a = (float)fabs(rno_bf16_to_double(normed[r * ldn + j]));
+                if (a > amax) amax = a;
+            }
+            float s = amax / 448.0f;                       /* IEEE fp32 division */
+            if (scale) scale[k * scale_ld + r] = s;
+            if (codes) {
+                for (int64_t j = 128 * k; j < 128 * k + 128; ++j) {
+                    float n = (float)rno_bf16_to_double(normed[r * ldn + j]);
+                    uint8_t q;
+                    if (s == 0.0f)
+                        q = 0x00;                          /* all-zero block */
+                    else
+                        q = rno_float_to_e4m3(n / s);      /* IEEE fp32 division */
+                    codes[r * ldq + j] = q;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fused residual add + RMSNorm + 1x128 FP8 block quant.                     */
+/* FlashInfer PR #4480 description: one pass emits the residual sum (in      */
+/* place), the bf16 normed output, the fp32 block scales and the e4m3 codes; */
+/* the codes are quantised from the bf16-rounded normed values.  h is the    */
+/* bf16 rounding of the exact sum x + r (reading R4); rstd and the normed    */
+/* value n = h*rstd*w are FP64, n_bf16 is n rounded once to bf16.            */
+/* Any output pointer may be NULL.                                           */
+/* ------------------------------------------------------------------------ */
+
+int rno_add_rmsnorm_fp8(const uint16_t* x, int64_t ldx,
+                        const uint16_t* res, int64_t ldr,
+                        const uint16_t* w,
+                        int64_t T, int64_t H, float eps,
+                        uint16_t* h_out, int64_t ldh,
+                        double* rstd,
+                        double* normed, int64_t ldn,
+                        uint16_t* normed_bf16, int64_t ldnb,
+                        float* scale, int64_t scale_ld,
+                        uint8_t* codes, int64_t ldq)
+{
+    if (T < 0 || H <= 0 || H % 128 != 0 || scale_ld < T) return 1;
+    for (int64_t r = 0; r < T; ++r) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double s = rno_bf16_to_double(x[r * ldx + j]) + rno_bf16_to_double(res[r * ldr + j]);
+            uint16_t hb = rno_double_to_bf16(s);
+            if (h_out) h_out[r * ldh + j] = hb;
+            double hv = rno_bf16_to_double(hb);
+            ss += hv * hv;
+        }
+        double rs = 1.0 / sqrt(ss / (double)H + (double)eps);
+        if (rstd) rstd[r] = rs;
+        for (int64_t j = 0; j < H; ++j) {
+            double s = rno_bf16_to_double(x[r * ldx + j]) + rno_bf16_to_double(res[r * ldr + j]);
+            double hv = rno_bf16_to_double(rno_double_to_bf16(s));
+            double n = hv * rs * rno_bf16_to_double(w[j]);
+            if (normed) normed[r * ldn + j] = n;
+            if (normed_bf16) normed_bf16[r * ldnb + j] = rno_double_to_bf16(n);
+        }
+        if (scale || codes) {
+            /* quantise this row from its own bf16 normed values */
+            uint16_t* row = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
+            if (!row) return 2;
+            for (int64_t j = 0; j < H; ++j) {
+                double s = rno_bf16_to_double(x[r * ldx + j]) + rno_bf16_to_double(res[r * ldr + j]);
+                double hv = rno_bf16_to_double(rno_double_to_bf16(s));
+                row[j] = rno_double_to_bf16(hv * rs * rno_bf16_to_double(w[j]));
+            }
+            int rc = rno_block_quant_e4m3(row, H, 1, H,
+                                          scale ? scale + r : NULL, scale_ld,
+                                          codes ? codes + r * ldq : NULL, ldq);
+            free(row);
+            if (rc) return rc;
+        }
+    }
+    return 0;
+}
