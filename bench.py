@@ -1,0 +1,241 @@
+"""Throughput of the RMSNorm hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic bf16
+activations, T = 8192 rows of H = 4096:
+    rmsnorm_fwd                   (x -> y, rstd)
+    rmsnorm_bwd, deterministic    (dy, x, rstd -> dx, dw)
+    add_rmsnorm_fp8_block_quant   (x, residual -> residual, normed, e4m3, scales)
+Each op reads its own buffers, and two buffer sets alternate between steps
+(1.3 GB in flight), so no op finds its inputs in the 256 MB Infinity Cache
+left by the op before it; inputs are resident in HBM when timing starts.
+
+value = algorithmic bytes of a step / wall time per step (GB/s).  Algorithmic
+bytes count each tensor once (weight once, not per row):
+    fwd  2*T*H*2 + 2*H + 4*T
+    bwd  3*T*H*2 + 2*H + 4*T + 4*H
+    fp8  9*T*H + 2*H + 4*(H/128)*round_up(T,4)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RMSNorm fwd+bwd & add-RMSNorm-FP8: achieved HBM GB/s, % of peak"
+HBM_PEAK_GBS = 8000.0
+T_ROWS, HIDDEN, EPS = 8192, 4096, 1e-6
+COUNTERS = os.path.join(ROOT, "profiles", "counters_T8192_H4096.json")
+KERNEL_SOURCES = {
+    "fwd": ["bwd_fp8_block_amd/csrc/rn_fwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
+    "bwd": ["bwd_fp8_block_amd/csrc/rn_bwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
+    "fp8": ["bwd_fp8_block_amd/csrc/rn_fp8.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
+}
+KERNEL_NAMES = {"fwd": "k_rmsnorm_fwd", "bwd": "k_rmsnorm_bwd + k_dw_reduce", "fp8": "k_add_rmsnorm_fp8"}
+
+
+def algorithmic_bytes(T, H):
+    ru4 = (T + 3) // 4 * 4
+    return {
+        "fwd": 2 * T * H * 2 + 2 * H + 4 * T,
+        "bwd": 3 * T * H * 2 + 2 * H + 4 * T + 4 * H,
+        "fp8": 9 * T * H + 2 * H + 4 * (H // 128) * ru4,
+    }
+
+
+def source_hash(op):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[op]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_set(torch, gen, dev, T, H, rn):
+    """One set of buffers for the three ops (each op has its own inputs)."""
+    bf = torch.bfloat16
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * scale).to(bf)
+
+    s = {}
+    s["w"] = (1.0 + 0.1 * torch.randn(H, generator=gen, device=dev)).to(bf)
+    s["x1"] = randn(T, H)
+    s["y1"] = torch.empty(T, H, dtype=bf, device=dev)
+    s["r1"] = torch.empty(T, dtype=torch.float32, device=dev)
+    s["x2"] = randn(T, H)
+    s["dy2"] = randn(T, H)
+    s["r2"] = torch.empty(T, dtype=torch.float32, device=dev)
+    s["dx2"] = torch.empty(T, H, dtype=bf, device=dev)
+    s["dw2"] = torch.empty(H, dtype=torch.float32, device=dev)
+    s["ws2"] = torch.empty(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4, dtype=torch.float32, device=dev)
+    s["x3"] = randn(T, H)
+    s["res3"] = randn(T, H)
+    s["out3"] = torch.empty(T, H, dtype=torch.uint8, device=dev)
+    s["sc3"] = torch.empty(H // 128, (T + 3) // 4 * 4, dtype=torch.float32, device=dev)
+    s["n3"] = torch.empty(T, H, dtype=bf, device=dev)
+    # the backward's rstd comes from a forward over its own x
+    tmp = torch.empty(T, H, dtype=bf, device=dev)
+    rn.rmsnorm_fwd(s["x2"], s["w"], tmp, s["r2"], EPS)
+    del tmp
+    return s
+
+
+def run_step(rn, s, ev=None):
+    if ev is not None:
+        ev[0].record()
+    rn.rmsnorm_fwd(s["x1"], s["w"], s["y1"], s["r1"], EPS)
+    if ev is not None:
+        ev[1].record()
+    rn.rmsnorm_bwd(s["dy2"], s["x2"], s["w"], s["r2"], s["dx2"], s["dw2"], deterministic=True, workspace=s["ws2"])
+    if ev is not None:
+        ev[2].record()
+    rn.add_rmsnorm_fp8_block_quant(s["x3"], s["res3"], s["w"], s["out3"], s["sc3"], s["n3"], EPS)
+    if ev is not None:
+        ev[3].record()
+
+
+def cpu_baseline(T, H):
+    """The CPU oracle on one full step's worth of rows (single thread), in GB/s of
+    the same algorithmic bytes."""
+    import numpy as np
+    import oracle
+    from workloads import Workload, generate
+    d = generate(Workload("cpu_sample", T, H, "bf16", "bf16", residual=True, seed=9090))
+    t0 = time.perf_counter()
+    _, rstd = oracle.rmsnorm_fwd(d["x"], d["w"], EPS)
+    t1 = time.perf_counter()
+    oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float32).astype(np.float64))
+    t2 = time.perf_counter()
+    oracle.add_rmsnorm_fp8(d["x"], d["residual"], d["w"], EPS)
+    t3 = time.perf_counter()
+    b = algorithmic_bytes(T, H)
+    total = sum(b.values())
+    return {
+        "value": round(total / (t3 - t0) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "one step: fwd + bwd + fused fp8 producer over T=%d rows of H=%d (bf16), single-threaded "
+                  "FP64 C oracle, %.1f s (fwd %.1f s, bwd %.1f s, fp8 %.1f s)" % (T, H, t3 - t0, t1 - t0,
+                                                                                  t2 - t1, t3 - t2),
+    }
+
+
+def counters_for(op):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current source of that kernel."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    e = c.get("ops", {}).get(op)
+    if not e or e.get("source_hash") != source_hash(op):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the RMSNorm path on a single MI355X and has "
+              "no multi-GPU mode (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bwd_fp8_block_amd as rn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, H = T_ROWS, HIDDEN
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261202)
+    sets = [make_set(torch, gen, dev, T, H, rn) for _ in range(2)]
+    torch.cuda.synchronize()
+
+    if args.calibration_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for i in range(args.warmup):
+        run_step(rn, sets[i % 2])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        run_step(rn, sets[i % 2], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    per = {"fwd": 0.0, "bwd": 0.0, "fp8": 0.0}
+    for e in evs:
+        per["fwd"] += e[0].elapsed_time(e[1])
+        per["bwd"] += e[1].elapsed_time(e[2])
+        per["fp8"] += e[2].elapsed_time(e[3])
+    per = {k: v / K for k, v in per.items()}           # ms per launch
+    b = algorithmic_bytes(T, H)
+    total = sum(b.values())
+    value = total / (ms_per_step * 1e-3) / 1e9
+    ops = {}
+    for k in per:
+        gbs = b[k] / (per[k] * 1e-3) / 1e9
+        ops[k] = {"kernel": KERNEL_NAMES[k], "bytes": b[k], "us": round(per[k] * 1e3, 3),
+                  "GB/s": round(gbs, 1), "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    dom = max(per, key=per.get)
+    achieved = b[dom] / (per[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counters_for(dom)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(T, H)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "rmsnorm fwd + fused bwd (deterministic dw) + add-rmsnorm-fp8 1x128 block quant, "
+                               "bf16 T=8192 H=4096", "T": T, "H": H, "eps": EPS,
+                   "bytes_per_step": total, "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "ops": ops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+"""MI355X (gfx950) RMSNorm: forward, fused dX+dW backward, and the fused
+residual-add + RMSNorm + FP8 e4m3 1x128 block-quant producer.
+
+Thin ctypes binding over ``librmsnorm_gfx950.so``, whose C ABI is declared in
+``include/rmsnorm_gfx950.h``.  Each function here only marshals arguments:
+it checks that the torch tensors live on the current GPU with contiguous
+columns, passes raw device pointers, row strides and torch's current HIP
+stream to the C entry point of the same name, and raises ``RNError`` on a
+non-zero status.  All arithmetic runs in the library's HIP kernels; there is
+no other code path, and importing this package fails loudly when the library
+has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RNError", "RN_F32", "RN_BF16", "RN_MAX_H", "lib", "library_path",
+    "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes", "add_rmsnorm_fp8_block_quant",
+    "rn_query_policy", "rn_bwd_workspace_bytes_for", "rn_status_string", "rn_version",
+    "rn_selftest_quant", "rn_selftest_cvt_e4m3",
+]
+
+RN_F32 = 0
+RN_BF16 = 1
+RN_MAX_H = 32768
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "librmsnorm_gfx950.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        "bwd_fp8_block_amd: %s is missing; build it with `python -m bwd_fp8_block_amd.build` "
+        "(or __graft_entry__.build())" % library_path)
+
+# torch is imported first so that its HIP runtime is the one the library binds to.
+lib = ctypes.CDLL(library_path)
+
+_i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+lib.rn_status_string.argtypes = [_i32]
+lib.rn_status_string.restype = ctypes.c_char_p
+lib.rn_version.argtypes = []
+lib.rn_version.restype = _i32
+lib.rmsnorm_fwd.argtypes = [_vp, _i64, _i32, _vp, _i32, _vp, _i64, _vp, _i64, _i64, _f32, _vp]
+lib.rmsnorm_fwd.restype = _i32
+lib.rmsnorm_bwd_workspace_bytes.argtypes = [_i64, _i64, _i32]
+lib.rmsnorm_bwd_workspace_bytes.restype = _sz
+lib.rmsnorm_bwd.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp,
+                            _i64, _i64, _i32, _vp, _sz, _vp]
+lib.rmsnorm_bwd.restype = _i32
+lib.add_rmsnorm_fp8_block_quant.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64,
+                                            _i64, _i64, _f32, _vp]
+lib.add_rmsnorm_fp8_block_quant.restype = _i32
+lib.rn_query_policy.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]
+lib.rn_query_policy.restype = _i32
+lib.rn_bwd_workspace_bytes_for.argtypes = [_i64, _i64, _i32]
+lib.rn_bwd_workspace_bytes_for.restype = _sz
+lib.rn_selftest_quant.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp]
+lib.rn_selftest_quant.restype = _i32
+lib.rn_selftest_cvt_e4m3.argtypes = [_vp, _vp, _i64, _vp]
+lib.rn_selftest_cvt_e4m3.restype = _i32
+
+_SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+class RNError(RuntimeError):
+    """A non-zero rn_status returned by the library."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (fn, rn_status_string(status), status))
+
+
+def rn_status_string(status: int) -> str:
+    return lib.rn_status_string(int(status)).decode()
+
+
+def rn_version() -> int:
+    return int(lib.rn_version())
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise RNError(fn, st)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RN_BF16
+    if t.dtype == torch.float32:
+        return RN_F32
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _dev(tensors) -> torch.device:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (got %s)" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors are on different devices")
+    return dev
+
+
+def _mat(t: torch.Tensor, name: str):
+    """(pointer, row stride in elements) of a 2-D tensor with contiguous columns."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D [T, H]" % name)
+    if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have contiguous columns" % name)
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return t.data_ptr(), ld
+
+
+def _vec(t: torch.Tensor, name: str):
+    if t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+        raise ValueError("%s must be a contiguous 1-D tensor" % name)
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.Tensor, eps: float) -> None:
+    """y = x * rstd * w with rstd = 1/sqrt(mean(x^2) + eps); writes y [T,H] and rstd [T] (fp32)."""
+    dev = _dev((x, w, y, rstd))
+    T, H = x.shape
+    if y.shape != x.shape or y.dtype != x.dtype or w.shape != (H,) or rstd.shape != (T,) or rstd.dtype != torch.float32:
+        raise ValueError("rmsnorm_fwd: shape or dtype mismatch")
+    px, ldx = _mat(x, "x")
+    py, ldy = _mat(y, "y")
+    with torch.cuda.device(dev):
+        st = lib.rmsnorm_fwd(px, ldx, _dt(x), _vec(w, "w"), _dt(w), py, ldy, _vec(rstd, "rstd"),
+                             T, H, float(eps), _stream(dev))
+    _check("rmsnorm_fwd", st)
+
+
+def rmsnorm_bwd_workspace_bytes(T: int, H: int, device=None) -> int:
+    """Workspace bytes a deterministic rmsnorm_bwd needs for (T, H) on `device`."""
+    if device is None:
+        device = torch.cuda.current_device()
+    idx = torch.device(device).index if not isinstance(device, int) else device
+    if idx is None:
+        idx = torch.cuda.current_device()
+    n = lib.rmsnorm_bwd_workspace_bytes(int(T), int(H), int(idx))
+    if n == _SIZE_MAX:
+        raise RNError("rmsnorm_bwd_workspace_bytes", 2)
+    return int(n)
+
+
+def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor,
+                dx: torch.Tensor, dw: torch.Tensor, deterministic: bool = True,
+                workspace: torch.Tensor | None = None) -> None:
+    """dx [T,H] and dw [H] (fp32, overwritten) from dy, x, w and the forward's rstd."""
+    dev = _dev((dy, x, w, rstd, dx, dw, workspace))
+    T, H = x.shape
+    if dy.shape != x.shape or dx.shape != x.shape or dy.dtype != x.dtype or dx.dtype != x.dtype:
+        raise ValueError("rmsnorm_bwd: dy/x/dx shape or dtype mismatch")
+    if w.shape != (H,) or rstd.shape != (T,) or dw.shape != (H,) or dw.dtype != torch.float32:
+        raise ValueError("rmsnorm_bwd: w/rstd/dw shape or dtype mismatch")
+    pdy, lddy = _mat(dy, "dy")
+    px, ldx = _mat(x, "x")
+    pdx, lddx = _mat(dx, "dx")
+    wsp, wsb = None, 0
+    if workspace is not None:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.rmsnorm_bwd(pdy, lddy, px, ldx, _dt(x), _vec(w, "w"), _dt(w), _vec(rstd, "rstd"),
+                             pdx, lddx, _vec(dw, "dw"), T, H, 1 if deterministic else 0, wsp, wsb, _stream(dev))
+    _check("rmsnorm_bwd", st)
+
+
+def add_rmsnorm_fp8_block_quant(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor,
+                                out: torch.Tensor, block_scale: torch.Tensor, normed_out: torch.Tensor,
+                                eps: float) -> None:
+    """residual <- bf16(x + residual); normed_out = bf16 RMSNorm(residual) * w;
+    out = e4m3 codes [T,H] (uint8 or float8_e4m3fn); block_scale [H/128, ld] fp32 with
+    entry (k, m) the scale of row m, block k (ld = block_scale.stride(0) >= T)."""
+    dev = _dev((x, residual, w, out, block_scale, normed_out))
+    T, H = x.shape
+    for t, n in ((x, "x"), (residual, "residual"), (w, "w"), (normed_out, "normed_out")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16" % n)
+    if out.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("out must be uint8 or float8_e4m3fn")
+    if residual.shape != x.shape or normed_out.shape != x.shape or out.shape != x.shape or w.shape != (H,):
+        raise ValueError("add_rmsnorm_fp8_block_quant: shape mismatch")
+    if block_scale.dtype != torch.float32 or block_scale.dim() != 2 or block_scale.shape[0] != H // 128:
+        raise ValueError("block_scale must be float32 [H/128, >= T]")
+    if block_scale.shape[1] < T or (block_scale.numel() > 1 and block_scale.stride(1) != 1):
+        raise ValueError("block_scale must be [H/128, ld >= T] with the row index contiguous")
+    scale_ld = block_scale.stride(0) if block_scale.shape[0] > 1 else block_scale.shape[1]
+    px, ldx = _mat(x, "x")
+    pr, ldr = _mat(residual, "residual")
+    po, ldo = _mat(out, "out")
+    pn, ldn = _mat(normed_out, "normed_out")
+    with torch.cuda.device(dev):
+        st = lib.add_rmsnorm_fp8_block_quant(px, ldx, pr, ldr, _vec(w, "w"), po, ldo,
+                                             block_scale.data_ptr(), scale_ld, pn, ldn,
+                                             T, H, float(eps), _stream(dev))
+    _check("add_rmsnorm_fp8_block_quant", st)
+
+
+def rn_query_policy(op: int, T: int, H: int, x_dtype: int, w_dtype: int, cu_count: int) -> dict:
+    """Host-only launch policy (no GPU needed)."""
+    out = (ctypes.c_int32 * 6)()
+    _check("rn_query_policy", lib.rn_query_policy(op, T, H, x_dtype, w_dtype, cu_count, out))
+    return dict(lpr=out[0], nv=out[1], wgs=out[2], grid=out[3], gpw=out[4], kernel=out[5])
+
+
+def rn_bwd_workspace_bytes_for(T: int, H: int, cu_count: int) -> int:
+    n = lib.rn_bwd_workspace_bytes_for(int(T), int(H), int(cu_count))
+    if n == _SIZE_MAX:
+        raise RNError("rn_bwd_workspace_bytes_for", 2)
+    return int(n)
+
+
+def rn_selftest_quant(a_lo: int, a_hi: int, mismatches: torch.Tensor, first_bad: torch.Tensor) -> None:
+    """Exhaustive check of the producer's quantisation step (see the C header)."""
+    dev = _dev((mismatches, first_bad))
+    with torch.cuda.device(dev):
+        st = lib.rn_selftest_quant(a_lo, a_hi, mismatches.data_ptr(), first_bad.data_ptr(), _stream(dev))
+    _check("rn_selftest_quant", st)
+
+
+def rn_selftest_cvt_e4m3(x: torch.Tensor, out: torch.Tensor) -> None:
+    """out[i] = e4m3 code of float32 x[i], via the producer's conversion instruction."""
+    dev = _dev((x, out))
+    if x.dtype != torch.float32 or out.dtype != torch.uint8 or x.numel() != out.numel():
+        raise ValueError("rn_selftest_cvt_e4m3: float32 in, uint8 out, same size")
+    with torch.cuda.device(dev):
+        st = lib.rn_selftest_cvt_e4m3(x.data_ptr(), out.data_ptr(), x.numel(), _stream(dev))
+    _check("rn_selftest_cvt_e4m3", st)

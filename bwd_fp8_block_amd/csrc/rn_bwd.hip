@@ -1,0 +1,290 @@
+// rn_bwd.hip -- RMSNorm backward (dx and dw in one pass over the rows) for gfx950.
+//
+// Operation ([C] = FlashInfer commit #5741 "cake_rmsnorm_train", Design:
+// Backward and Determinism; [L] = Liger-Kernel PR #1336, the fused single-pass
+// dX+dW strip-reduction backward):
+//   xhat = x * rstd;  c = mean_j(g * w * xhat);  dx = rstd * (g*w - c*xhat)
+//   dw_j = sum over rows of g * x * rstd
+//
+// Mapping.  The rows are split into G contiguous chunks, one per work-group
+// ("strips").  A work-group holds GPW row groups of LPR lanes; each row group
+// walks every GPW-th row of the strip.  Per row: 16-byte loads of g and x,
+// fp32 dot product reduced across the row group (DPP, then LDS when a row
+// spans several wavefronts), dx written back, and the dw contribution of the
+// row added to per-lane FP64 accumulators for the lane's columns.
+//
+// dw accuracy.  For bf16 inputs g*x is exact in fp32 (8 + 8 significant
+// bits), and (g*x)*rstd is exact in FP64 (16 + 24 bits), so each contribution
+// enters the FP64 accumulator exactly; the only roundings of a strip partial
+// are FP64 additions and the final fp32 rounding.  On the pages' hardware
+// the same budget (every element within 1e-4 + 1e-4*|ref| of an FP64 sum,
+// miles-ext-kernels PR #15, Summary) is met with compensated fp32 sums; on
+// gfx950 FP64 FMA issues at the same rate as fp32 FMA, so plain FP64
+// accumulation is the cheaper way to the same end.
+//
+// Deterministic mode: each strip writes its fp32 partial row to the
+// workspace, and a second kernel sums the G partials of every column in a
+// fixed order in FP64 (no atomics: the result depends only on T, H and G).
+// Non-deterministic mode: dw is zeroed by a fill kernel and each strip adds
+// its partial with hardware fp32 atomics.
+#include "rn_device.h"
+#include "rn_internal.h"
+
+namespace rn {
+
+template <int NV>
+__device__ __forceinline__ void bwd_load_row(u32x4 (&v)[NV], const u32x4* row, int lane, int lpr, int nch, bool valid)
+{
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + lpr * i;
+        if (valid && c < nch) v[i] = row[c];
+        else v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET>
+__global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
+{
+    constexpr int E = Elems<XT>::value;
+    constexpr int XB = (XT == DT_BF16) ? 2 : 4;
+    constexpr int WPER = (WT == DT_F32) ? 4 : 8;    // w values per 16-byte word
+    constexpr int WCH = E / WPER;                   // w words per x chunk
+    constexpr int HALF = E / 2;                     // accumulators staged per LDS pass
+
+    __shared__ float red[2][16];
+    __shared__ double stage[WGMAX * HALF];
+
+    const Rows<LPRC> R(a.lpr);
+    const int lane = R.lane, lpr = R.lpr, gpw = R.gpw;
+    const int tid = threadIdx.x;
+    const int nch = a.nch;
+    const int64_t G = gridDim.x;
+    const int64_t strip = xcd_chunk(blockIdx.x, G);
+
+    int64_t lo, hi;
+    chunk_rows(strip, G, a.T, lo, hi);
+    const int n_it = (int)((hi - lo + gpw - 1) / gpw);
+
+    // w for this lane's columns, fp32 in registers.
+    float wf[NV][E];
+    {
+        const u32x4* wp = static_cast<const u32x4*>(a.w);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + lpr * i;
+#pragma unroll
+            for (int k = 0; k < WCH; ++k) {
+                u32x4 v = (c < nch) ? wp[c * WCH + k] : u32x4{0u, 0u, 0u, 0u};
+                unpack<WT>(v, &wf[i][k * WPER]);
+            }
+        }
+    }
+
+    double acc[NV][E];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[i][e] = 0.0;
+
+    const char* gbase = static_cast<const char*>(a.dy);
+    const char* xbase = static_cast<const char*>(a.x);
+    char* dxbase = static_cast<char*>(a.dx);
+
+    // Software pipeline: the next row's g, x and rstd are loaded while the
+    // current row is reduced and written.
+    u32x4 gn[NV], xn[NV];
+    float rsn;
+    {
+        const int64_t r0 = lo + R.grp;
+        const bool v0 = r0 < hi;
+        bwd_load_row<NV>(gn, reinterpret_cast<const u32x4*>(gbase + r0 * a.lddy * XB), lane, lpr, nch, v0);
+        bwd_load_row<NV>(xn, reinterpret_cast<const u32x4*>(xbase + r0 * a.ldx * XB), lane, lpr, nch, v0);
+        rsn = v0 ? a.rstd[r0] : 0.0f;
+    }
+
+    for (int it = 0; it < n_it; ++it) {
+        const int64_t r = lo + R.grp + (int64_t)it * gpw;
+        const bool valid = r < hi;
+        u32x4 gv[NV], xv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) { gv[i] = gn[i]; xv[i] = xn[i]; }
+        const float rs = rsn;
+        if (it + 1 < n_it) {
+            const int64_t rn = r + gpw;
+            const bool vn = rn < hi;
+            bwd_load_row<NV>(gn, reinterpret_cast<const u32x4*>(gbase + rn * a.lddy * XB), lane, lpr, nch, vn);
+            bwd_load_row<NV>(xn, reinterpret_cast<const u32x4*>(xbase + rn * a.ldx * XB), lane, lpr, nch, vn);
+            rsn = vn ? a.rstd[rn] : 0.0f;
+        }
+
+        // dot = sum_j g*w*xhat, and the exact dw contributions of this row.
+        const double rsd = (double)rs;
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float g[E], x[E];
+            unpack<XT>(gv[i], g);
+            unpack<XT>(xv[i], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                dot = __builtin_fmaf(g[e] * wf[i][e], x[e] * rs, dot);
+                if constexpr (XT == DT_BF16)
+                    acc[i][e] = __builtin_fma((double)(g[e] * x[e]), rsd, acc[i][e]);
+                else
+                    acc[i][e] = __builtin_fma((double)g[e] * (double)x[e], rsd, acc[i][e]);
+            }
+        }
+        dot = R.sum(dot, red, it);
+        const float cm = dot / (float)a.H;
+
+        u32x4* dxrow = reinterpret_cast<u32x4*>(dxbase + r * a.lddx * XB);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + lpr * i;
+            float g[E], x[E], o[E];
+            unpack<XT>(gv[i], g);
+            unpack<XT>(xv[i], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = rs * __builtin_fmaf(-cm, x[e] * rs, g[e] * wf[i][e]);
+            if (valid && c < nch) dxrow[c] = pack<XT>(o);
+        }
+    }
+
+    // Emit this strip's dw partial: the gpw row groups' accumulators are
+    // combined in a fixed order (group 0, 1, ...) in FP64 and rounded once to
+    // fp32.  Staged through LDS, HALF values per lane per pass.
+    float* part = a.part;
+    if (gpw == 1) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + lpr * i;
+            if (c < nch) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float p = (float)acc[i][e];
+                    const int64_t col = (int64_t)c * E + e;
+                    if constexpr (DET) part[strip * a.H + col] = p;
+                    else unsafeAtomicAdd(&part[col], p);
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+        for (int h0 = 0; h0 < E; h0 += HALF) {
+#pragma unroll
+            for (int e = 0; e < HALF; ++e) stage[tid * HALF + e] = acc[i][h0 + e];
+            __syncthreads();
+            for (int v = tid; v < lpr * HALF; v += blockDim.x) {
+                const int l = v / HALF, e = v - l * HALF;
+                const int c = l + lpr * i;
+                if (c < nch) {
+                    double s = 0.0;
+                    for (int q = 0; q < gpw; ++q) s += stage[(q * lpr + l) * HALF + e];
+                    const float p = (float)s;
+                    const int64_t col = (int64_t)c * E + h0 + e;
+                    if constexpr (DET) part[strip * a.H + col] = p;
+                    else unsafeAtomicAdd(&part[col], p);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// dw[j] = fp32( sum over g = 0..G-1 of part[g][j] ), FP64, fixed order: the 16
+// wavefronts of a work-group sum contiguous ranges of g in order, then the 16
+// range sums are added in wavefront order.  One lane per column.
+__global__ __launch_bounds__(1024) void k_dw_reduce(ReduceArgs a)
+{
+    constexpr int NW = 16;
+    __shared__ double red[NW][64];
+    const int wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t g0 = (wv * a.G) / NW, g1 = ((wv + 1) * a.G) / NW;
+    double s = 0.0;
+    if (col < a.H) {
+        const float* p = a.part + col;
+#pragma unroll 8
+        for (int64_t g = g0; g < g1; ++g) s += (double)p[g * a.H];
+    }
+    red[wv][lane] = s;
+    __syncthreads();
+    if (wv == 0 && col < a.H) {
+        double t = 0.0;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) t += red[k][lane];
+        a.dw[col] = (float)t;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Variant table and dispatch.
+// ---------------------------------------------------------------------------
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET>
+static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    return hipGetLastError();
+}
+
+// (group class, vectors per lane, largest work-group) triples compiled.
+#define RN_BWD_VARIANTS(X) X(16, 1, 1024) X(32, 1, 1024) X(64, 1, 1024) X(64, 2, 1024)
+
+bool bwd_variant_exists(int lprc, int nv, int wgs)
+{
+#define X(C, N, W) if (lprc == C && nv == N && wgs <= W) return true;
+    RN_BWD_VARIANTS(X)
+#undef X
+    return false;
+}
+
+template <int XT, int WT, bool DET>
+static hipError_t bwd_dispatch(const BwdArgs& a, const Policy& p, hipStream_t s)
+{
+    const int lprc = p.lpr < 64 ? p.lpr : 64;
+#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return bwd_go<XT, WT, C, N, W, DET>(a, p, s);
+    RN_BWD_VARIANTS(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, bool det, const Policy& p, hipStream_t s)
+{
+    if (det) {
+        if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16, true>(a, p, s);
+        if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32, true>(a, p, s);
+        if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32, true>(a, p, s);
+    } else {
+        if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16, false>(a, p, s);
+        if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32, false>(a, p, s);
+        if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32, false>(a, p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((a.H + 63) / 64);
+    hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(1024), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(k_fill_zero, dim3(grid), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+} // namespace rn

@@ -1,0 +1,461 @@
+// rn_host.hip -- C ABI of the gfx950 RMSNorm library: argument validation,
+// launch policy and enqueue.  Never allocates, never synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/rmsnorm_gfx950.h"
+#include "rn_internal.h"
+
+using rn::Policy;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Per-device property cache (the only global state).
+// ---------------------------------------------------------------------------
+struct DevInfo {
+    std::atomic<int> state{0};   // 0 unknown, 1 ok, 2 not gfx950 / error
+    int cu = 0;
+};
+constexpr int kMaxDev = 64;
+DevInfo g_dev[kMaxDev];
+std::mutex g_dev_mu;
+
+int device_cu(int dev, int* cu)
+{
+    if (dev < 0 || dev >= kMaxDev) return RN_ERR_DEVICE;
+    DevInfo& d = g_dev[dev];
+    int st = d.state.load(std::memory_order_acquire);
+    if (st == 0) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        st = d.state.load(std::memory_order_relaxed);
+        if (st == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+                st = 2;
+            } else {
+                st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.multiProcessorCount > 0) ? 1 : 2;
+                d.cu = prop.multiProcessorCount;
+            }
+            d.state.store(st, std::memory_order_release);
+        }
+    }
+    if (st != 1) return RN_ERR_DEVICE;
+    *cu = d.cu;
+    return RN_OK;
+}
+
+int current_device_cu(int* cu)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return RN_ERR_DEVICE;
+    return device_cu(dev, cu);
+}
+
+// ---------------------------------------------------------------------------
+// Optional policy override for tuning sweeps, read once: RN_POLICY_FWD,
+// RN_POLICY_BWD, RN_POLICY_FP8 = "lpr,nv,wgs,grid" (0 keeps the default).
+// ---------------------------------------------------------------------------
+struct Override { int lpr = 0, nv = 0, wgs = 0; long long grid = 0; };
+Override g_ovr[3];
+std::once_flag g_ovr_once;
+bool g_log = false;
+
+void read_overrides()
+{
+    const char* names[3] = {"RN_POLICY_FWD", "RN_POLICY_BWD", "RN_POLICY_FP8"};
+    for (int k = 0; k < 3; ++k) {
+        const char* v = std::getenv(names[k]);
+        if (v) std::sscanf(v, "%d,%d,%d,%lld", &g_ovr[k].lpr, &g_ovr[k].nv, &g_ovr[k].wgs, &g_ovr[k].grid);
+    }
+    const char* l = std::getenv("RN_LOG");
+    g_log = l && l[0] == '1';
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Threads per work-group for a row-group width: as many whole groups as fit
+// in `cap` threads.
+int wgs_for(int lpr, int cap) { return lpr >= cap ? lpr : lpr * (cap / lpr); }
+
+int elems_per_chunk(int dt) { return dt == RN_BF16 ? 8 : 4; }
+int elem_bytes(int dt) { return dt == RN_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------
+// Launch policies (pure functions of the shape and the CU count).
+// ---------------------------------------------------------------------------
+
+// Forward: a row group holds up to 8 vectors of 16 bytes per lane; one row
+// per wavefront up to 8 KiB rows (H = 4096 bf16), narrower groups for short
+// rows, several wavefronts per row beyond.  Up to 32 wavefronts per CU.
+int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
+{
+    const int nch = (int)(H / elems_per_chunk(x_dtype));
+    if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
+    else if (nch <= 32)   { p->lpr = 16; p->nv = 2; }
+    else if (nch <= 64)   { p->lpr = 16; p->nv = 4; }
+    else if (nch <= 128)  { p->lpr = 32; p->nv = 4; }
+    else                  { p->lpr = 64 * (int)ceil_div(nch, 64 * 8); p->nv = (int)ceil_div(nch, p->lpr); }
+    if (p->lpr > 512) return RN_ERR_SHAPE;
+    p->wgs = wgs_for(p->lpr, 256);
+    p->gpw = p->wgs / p->lpr;
+    const int64_t per_cu = 2048 / p->wgs;
+    int64_t g = ceil_div(T, p->gpw);
+    if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
+    p->grid = g < 1 ? 1 : g;
+    p->kernel = 0;
+    return RN_OK;
+}
+
+// Backward: one vector (8 bf16 / 4 fp32 columns) per lane so that the FP64
+// dw accumulators stay in registers; a row spans ceil(H/chunk/64) wavefronts;
+// one 1024-thread work-group (one row strip) per CU.  Rows wider than 1024
+// vectors take two vectors per lane.
+int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
+{
+    const int nch = (int)(H / elems_per_chunk(x_dtype));
+    if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
+    else if (nch <= 32)   { p->lpr = 32; p->nv = 1; }
+    else if (nch <= 1024) { p->lpr = 64 * (int)ceil_div(nch, 64); p->nv = 1; }
+    else                  { p->lpr = 64 * (int)ceil_div(nch, 128); p->nv = 2; }
+    if (p->lpr > 1024) return RN_ERR_SHAPE;
+    p->wgs = wgs_for(p->lpr, 1024);
+    p->gpw = p->wgs / p->lpr;
+    int64_t g = ceil_div(T, p->gpw);
+    const int64_t per_cu = 1;
+    if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
+    p->grid = g < 1 ? 1 : g;
+    p->kernel = 1;
+    return RN_OK;
+}
+
+// Fused fp8 producer: a 1x128 block is 16 lanes, so groups are 16, 32 or a
+// multiple of 64 lanes, with up to 8 vectors per lane.
+int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
+{
+    const int nch = (int)(H / 8);
+    if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
+    else if (nch <= 32)   { p->lpr = 32; p->nv = 1; }
+    else                  { p->lpr = 64 * (int)ceil_div(nch, 64 * 8); p->nv = (int)ceil_div(nch, p->lpr); }
+    if (p->lpr > 512) return RN_ERR_SHAPE;
+    p->wgs = wgs_for(p->lpr, 256);
+    p->gpw = p->wgs / p->lpr;
+    const int64_t per_cu = 2048 / p->wgs;
+    int64_t g = ceil_div(T, p->gpw);
+    if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
+    p->grid = g < 1 ? 1 : g;
+    p->kernel = 2;
+    return RN_OK;
+}
+
+// Apply a tuning override; refuse anything that no compiled variant serves or
+// that breaks the geometry invariants (wgs a multiple of lpr, lpr % 64 == 0
+// beyond 32 lanes, 16-lane blocks for the fp8 kernel).
+void apply_override(int op, int64_t T, int nch, Policy* p)
+{
+    std::call_once(g_ovr_once, read_overrides);
+    const Override& o = g_ovr[op];
+    if (!o.lpr && !o.nv && !o.wgs && !o.grid) return;
+    Policy q = *p;
+    if (o.lpr) q.lpr = o.lpr;
+    if (o.nv) q.nv = o.nv;
+    if (o.wgs) q.wgs = o.wgs;
+    else q.wgs = wgs_for(q.lpr, op == 1 ? 1024 : 256);
+    if (q.lpr <= 0 || q.wgs <= 0 || q.wgs > 1024 || q.wgs % q.lpr != 0) return;
+    if (op == 2 && q.lpr % 16 != 0) return;
+    if (q.lpr != 16 && q.lpr != 32 && q.lpr % 64 != 0) return;
+    if ((int64_t)q.lpr * q.nv < nch) return;
+    q.gpw = q.wgs / q.lpr;
+    const int lprc = q.lpr < 64 ? q.lpr : 64;
+    const bool ok = op == 0 ? rn::fwd_variant_exists(lprc, q.nv, q.wgs)
+                  : op == 1 ? rn::bwd_variant_exists(lprc, q.nv, q.wgs)
+                            : rn::fp8_variant_exists(lprc, q.nv, q.wgs);
+    if (!ok) return;
+    if (o.grid) q.grid = o.grid;
+    else q.grid = std::max<int64_t>(1, std::min<int64_t>(p->grid * p->gpw / q.gpw, ceil_div(T, q.gpw)));
+    if (op == 1 && q.grid > p->grid) q.grid = p->grid;   // workspace is sized for the default
+    *p = q;
+}
+
+void log_policy(const char* op, int64_t T, int64_t H, const Policy& p)
+{
+    std::call_once(g_ovr_once, read_overrides);
+    if (g_log)
+        std::fprintf(stderr, "[rmsnorm_gfx950] %s T=%lld H=%lld lpr=%d nv=%d wgs=%d gpw=%d grid=%lld\n", op,
+                     (long long)T, (long long)H, p.lpr, p.nv, p.wgs, p.gpw, (long long)p.grid);
+}
+
+// ---------------------------------------------------------------------------
+// Validation helpers.
+// ---------------------------------------------------------------------------
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Extent {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Extent mat_extent(const void* p, int64_t T, int64_t H, int64_t ld, int64_t esize)
+{
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return {b, b + (uintptr_t)(((T - 1) * ld + H) * esize)};
+}
+
+Extent vec_extent(const void* p, int64_t n, int64_t esize)
+{
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return {b, b + (uintptr_t)(n * esize)};
+}
+
+bool overlap(const Extent& a, const Extent& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool valid_pair(int x_dtype, int w_dtype)
+{
+    return (x_dtype == RN_F32 && w_dtype == RN_F32) || (x_dtype == RN_BF16 && w_dtype == RN_BF16) ||
+           (x_dtype == RN_BF16 && w_dtype == RN_F32);
+}
+
+int check_matrix(const void* p, int64_t ld, int64_t H, int dt)
+{
+    if (!aligned(p, 16)) return RN_ERR_ALIGN;
+    if (ld < H || (ld * elem_bytes(dt)) % 16 != 0) return RN_ERR_STRIDE;
+    return RN_OK;
+}
+
+int check_h(int64_t H, int dt)
+{
+    if (H <= 0 || H > RN_MAX_H) return RN_ERR_SHAPE;
+    if (H % elems_per_chunk(dt) != 0) return RN_ERR_SHAPE;
+    return RN_OK;
+}
+
+// Clear a stale error left by earlier HIP calls on this thread, so that the
+// error read after our launch is our own.
+void clear_last_error() { (void)hipGetLastError(); }
+
+} // namespace
+
+// ===========================================================================
+// Exported C ABI.
+// ===========================================================================
+extern "C" {
+
+const char* rn_status_string(int status)
+{
+    switch (status) {
+    case RN_OK: return "ok";
+    case RN_ERR_NULL: return "null pointer";
+    case RN_ERR_SHAPE: return "unsupported shape";
+    case RN_ERR_DTYPE: return "unsupported dtype";
+    case RN_ERR_ALIGN: return "misaligned pointer";
+    case RN_ERR_STRIDE: return "bad row stride";
+    case RN_ERR_WORKSPACE: return "workspace missing or too small";
+    case RN_ERR_ALIAS: return "overlapping buffers";
+    case RN_ERR_DEVICE: return "no gfx950 device";
+    case RN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int rn_version(void) { return 10000; }
+
+int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype, int cu_count, int32_t* out)
+{
+    if (!out) return RN_ERR_NULL;
+    if (cu_count <= 0 || T < 0) return RN_ERR_SHAPE;
+    Policy p{};
+    int st;
+    if (op == 0 || op == 1) {
+        if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
+        if ((st = check_h(H, x_dtype)) != RN_OK) return st;
+        st = op == 0 ? policy_fwd(T, H, x_dtype, cu_count, &p) : policy_bwd(T, H, x_dtype, cu_count, &p);
+    } else if (op == 2) {
+        if (x_dtype != RN_BF16 || w_dtype != RN_BF16) return RN_ERR_DTYPE;
+        if (H <= 0 || H > RN_MAX_H || H % 128 != 0) return RN_ERR_SHAPE;
+        st = policy_fp8(T, H, cu_count, &p);
+    } else {
+        return RN_ERR_SHAPE;
+    }
+    if (st != RN_OK) return st;
+    out[0] = p.lpr; out[1] = p.nv; out[2] = p.wgs; out[3] = (int32_t)p.grid; out[4] = p.gpw; out[5] = p.kernel;
+    return RN_OK;
+}
+
+size_t rn_bwd_workspace_bytes_for(int64_t T, int64_t H, int cu_count)
+{
+    if (T < 0 || H <= 0 || H > RN_MAX_H || cu_count <= 0) return (size_t)-1;
+    if (T == 0) return 0;
+    Policy p{};
+    // The bf16 and f32 policies give the same strip count bound (<= cu_count);
+    // size for the larger of the two so one workspace serves both.
+    size_t best = 0;
+    for (int dt = 0; dt < 2; ++dt) {
+        if (H % elems_per_chunk(dt) != 0) continue;
+        if (policy_bwd(T, H, dt, cu_count, &p) != RN_OK) continue;
+        const size_t b = (size_t)p.grid * (size_t)H * sizeof(float);
+        if (b > best) best = b;
+    }
+    if (best == 0) return (size_t)-1;
+    return (best + 255) / 256 * 256;
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t H, int device)
+{
+    int cu = 0;
+    if (device_cu(device, &cu) != RN_OK) return (size_t)-1;
+    return rn_bwd_workspace_bytes_for(T, H, cu);
+}
+
+int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype, void* y, int64_t ldy,
+                float* rstd, int64_t T, int64_t H, float eps, void* stream)
+{
+    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
+    int st;
+    if ((st = check_h(H, x_dtype)) != RN_OK) return st;
+    if (T < 0) return RN_ERR_SHAPE;
+    Policy p{};
+    if ((st = policy_fwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
+    if (T == 0) return RN_OK;
+    if (!x || !w || !y || !rstd) return RN_ERR_NULL;
+    if ((st = check_matrix(x, ldx, H, x_dtype)) != RN_OK) return st;
+    if ((st = check_matrix(y, ldy, H, x_dtype)) != RN_OK) return st;
+    if (!aligned(w, 16) || !aligned(rstd, 4)) return RN_ERR_ALIGN;
+    const int xb = elem_bytes(x_dtype);
+    const Extent ex = mat_extent(x, T, H, ldx, xb), ey = mat_extent(y, T, H, ldy, xb);
+    const Extent ew = vec_extent(w, H, elem_bytes(w_dtype)), er = vec_extent(rstd, T, 4);
+    if (overlap(ey, ex) || overlap(ey, ew) || overlap(ey, er) || overlap(er, ex) || overlap(er, ew))
+        return RN_ERR_ALIAS;
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    if ((st = policy_fwd(T, H, x_dtype, cu, &p)) != RN_OK) return st;
+    apply_override(0, T, (int)(H / elems_per_chunk(x_dtype)), &p);
+    log_policy("fwd", T, H, p);
+
+    rn::FwdArgs a{};
+    a.lpr = p.lpr; a.x = x; a.ldx = ldx; a.w = w; a.y = y; a.ldy = ldy; a.rstd = rstd;
+    a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype)); a.eps = eps;
+    clear_last_error();
+    if (rn::launch_fwd(a, x_dtype, w_dtype, p, (hipStream_t)stream) != hipSuccess) return RN_ERR_LAUNCH;
+    return RN_OK;
+}
+
+int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype,
+                const float* rstd, void* dx, int64_t lddx, float* dw, int64_t T, int64_t H, int deterministic,
+                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
+    int st;
+    if ((st = check_h(H, x_dtype)) != RN_OK) return st;
+    if (T < 0) return RN_ERR_SHAPE;
+    Policy p{};
+    if ((st = policy_bwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
+    if (!dw) return RN_ERR_NULL;
+    if (!aligned(dw, 4)) return RN_ERR_ALIGN;
+    const int xb = elem_bytes(x_dtype);
+    const Extent edw = vec_extent(dw, H, 4);
+    Extent edy{}, ex{}, edx{}, ew{}, er{};
+    if (T > 0) {
+        if (!dy || !x || !w || !rstd || !dx) return RN_ERR_NULL;
+        if ((st = check_matrix(dy, lddy, H, x_dtype)) != RN_OK) return st;
+        if ((st = check_matrix(x, ldx, H, x_dtype)) != RN_OK) return st;
+        if ((st = check_matrix(dx, lddx, H, x_dtype)) != RN_OK) return st;
+        if (!aligned(w, 16) || !aligned(rstd, 4)) return RN_ERR_ALIGN;
+        edy = mat_extent(dy, T, H, lddy, xb);
+        ex = mat_extent(x, T, H, ldx, xb);
+        edx = mat_extent(dx, T, H, lddx, xb);
+        ew = vec_extent(w, H, elem_bytes(w_dtype));
+        er = vec_extent(rstd, T, 4);
+        if (overlap(edx, edy) || overlap(edx, ex) || overlap(edx, ew) || overlap(edx, er) || overlap(edx, edw) ||
+            overlap(edw, edy) || overlap(edw, ex) || overlap(edw, ew) || overlap(edw, er))
+            return RN_ERR_ALIAS;
+        if (deterministic && !workspace) return RN_ERR_WORKSPACE;
+        if (deterministic && !aligned(workspace, 16)) return RN_ERR_ALIGN;
+    }
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    clear_last_error();
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        // No rows: the weight gradient is the empty sum.
+        if (rn::launch_fill_zero(dw, H, s) != hipSuccess) return RN_ERR_LAUNCH;
+        return RN_OK;
+    }
+    if ((st = policy_bwd(T, H, x_dtype, cu, &p)) != RN_OK) return st;
+    const size_t need = (size_t)p.grid * (size_t)H * sizeof(float);
+    if (deterministic) {
+        if (workspace_bytes < need) return RN_ERR_WORKSPACE;
+        const Extent ews = vec_extent(workspace, (int64_t)(need / 4), 4);
+        if (overlap(ews, edy) || overlap(ews, ex) || overlap(ews, ew) || overlap(ews, er) || overlap(ews, edx) ||
+            overlap(ews, edw))
+            return RN_ERR_ALIAS;
+    }
+    apply_override(1, T, (int)(H / elems_per_chunk(x_dtype)), &p);
+    log_policy(deterministic ? "bwd(det)" : "bwd", T, H, p);
+
+    rn::BwdArgs a{};
+    a.lpr = p.lpr; a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.w = w; a.rstd = rstd;
+    a.dx = dx; a.lddx = lddx; a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype));
+    if (deterministic) {
+        a.part = static_cast<float*>(workspace);
+        if (rn::launch_bwd(a, x_dtype, w_dtype, true, p, s) != hipSuccess) return RN_ERR_LAUNCH;
+        rn::ReduceArgs ra{static_cast<const float*>(workspace), dw, p.grid, (int)H};
+        if (rn::launch_bwd_reduce(ra, s) != hipSuccess) return RN_ERR_LAUNCH;
+    } else {
+        a.part = dw;
+        if (rn::launch_fill_zero(dw, H, s) != hipSuccess) return RN_ERR_LAUNCH;
+        if (rn::launch_bwd(a, x_dtype, w_dtype, false, p, s) != hipSuccess) return RN_ERR_LAUNCH;
+    }
+    return RN_OK;
+}
+
+int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx, void* residual, int64_t ldr, const void* w,
+                                uint8_t* out, int64_t ldo, float* block_scale, int64_t scale_ld, void* normed_out,
+                                int64_t ldn, int64_t T, int64_t H, float eps, void* stream)
+{
+    if (H <= 0 || H > RN_MAX_H || H % 128 != 0) return RN_ERR_SHAPE;
+    if (T < 0) return RN_ERR_SHAPE;
+    int st;
+    Policy p{};
+    if ((st = policy_fp8(T, H, 1, &p)) != RN_OK) return st;               // shape range (CU-independent)
+    if (T == 0) return RN_OK;
+    if (!x || !residual || !w || !out || !block_scale || !normed_out) return RN_ERR_NULL;
+    if ((st = check_matrix(x, ldx, H, RN_BF16)) != RN_OK) return st;
+    if ((st = check_matrix(residual, ldr, H, RN_BF16)) != RN_OK) return st;
+    if ((st = check_matrix(normed_out, ldn, H, RN_BF16)) != RN_OK) return st;
+    if (!aligned(out, 16)) return RN_ERR_ALIGN;
+    if (ldo < H || ldo % 16 != 0) return RN_ERR_STRIDE;
+    if (!aligned(w, 16) || !aligned(block_scale, 4)) return RN_ERR_ALIGN;
+    if (scale_ld < T || scale_ld % 4 != 0) return RN_ERR_STRIDE;
+    const Extent ex = mat_extent(x, T, H, ldx, 2), er = mat_extent(residual, T, H, ldr, 2);
+    const Extent ew = vec_extent(w, H, 2), eo = mat_extent(out, T, H, ldo, 1);
+    const Extent en = mat_extent(normed_out, T, H, ldn, 2);
+    const Extent es = {reinterpret_cast<uintptr_t>(block_scale),
+                       reinterpret_cast<uintptr_t>(block_scale) + (uintptr_t)(((H / 128 - 1) * scale_ld + T) * 4)};
+    if (overlap(er, ex) || overlap(er, ew) || overlap(eo, ex) || overlap(eo, er) || overlap(eo, ew) ||
+        overlap(eo, en) || overlap(eo, es) || overlap(en, ex) || overlap(en, er) || overlap(en, ew) ||
+        overlap(en, es) || overlap(es, ex) || overlap(es, er) || overlap(es, ew))
+        return RN_ERR_ALIAS;
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    if ((st = policy_fp8(T, H, cu, &p)) != RN_OK) return st;
+    apply_override(2, T, (int)(H / 8), &p);
+    log_policy("fp8", T, H, p);
+
+    rn::Fp8Args a{};
+    a.lpr = p.lpr; a.x = x; a.ldx = ldx; a.res = residual; a.ldr = ldr; a.w = w; a.out = out; a.ldo = ldo;
+    a.scale = block_scale; a.scale_ld = scale_ld; a.normed = normed_out; a.ldn = ldn;
+    a.T = T; a.H = (int)H; a.nch = (int)(H / 8); a.eps = eps;
+    clear_last_error();
+    if (rn::launch_fp8(a, p, (hipStream_t)stream) != hipSuccess) return RN_ERR_LAUNCH;
+    return RN_OK;
+}
+
+} // extern "C"

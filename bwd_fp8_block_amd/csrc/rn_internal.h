@@ -1,0 +1,73 @@
+// rn_internal.h -- contract between the C-ABI host layer and the kernel
+// translation units: launch-policy record, kernel argument blocks and the
+// launcher entry points (C++ linkage, not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rn {
+
+// A launch policy, chosen on the host from (T, H, dtypes, CU count).
+struct Policy {
+    int lpr;        // lanes per row group: 16, 32, 64, 128, ..., 1024
+    int nv;         // 16-byte vectors per lane per row (compile-time variant)
+    int wgs;        // threads per work-group
+    int64_t grid;   // work-groups = row chunks
+    int gpw;        // row groups per work-group (rows processed per WG pass)
+    int kernel;     // variant id (for logging and tests)
+};
+
+struct FwdArgs {
+    int lpr;                     // lanes per row group (runtime for class 64)
+    const void* x; int64_t ldx;
+    const void* w;
+    void* y; int64_t ldy;
+    float* rstd;
+    int64_t T; int H; int nch;   // nch = H / elements-per-chunk
+    float eps;
+};
+
+struct BwdArgs {
+    int lpr;
+    const void* dy; int64_t lddy;
+    const void* x; int64_t ldx;
+    const void* w;
+    const float* rstd;
+    void* dx; int64_t lddx;
+    float* part;                 // det: workspace [grid][H]; non-det: dw [H]
+    int64_t T; int H; int nch;
+};
+
+struct ReduceArgs {
+    const float* part;           // [G][H]
+    float* dw;                   // [H]
+    int64_t G; int H;
+};
+
+struct Fp8Args {
+    int lpr;
+    const void* x; int64_t ldx;
+    void* res; int64_t ldr;
+    const void* w;
+    uint8_t* out; int64_t ldo;
+    float* scale; int64_t scale_ld;
+    void* normed; int64_t ldn;
+    int64_t T; int H; int nch;
+    float eps;
+};
+
+// Launchers return hipSuccess or the launch error.  They assume validated args.
+hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, bool det, const Policy& p, hipStream_t s);
+hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_fp8(const Fp8Args& a, const Policy& p, hipStream_t s);
+
+// Variant tables (which (lpr, nv) pairs are compiled) -- used by the policy.
+// lprc is the group class: lpr for lpr < 64, else 64.
+bool fwd_variant_exists(int lprc, int nv, int wgs);
+bool bwd_variant_exists(int lprc, int nv, int wgs);
+bool fp8_variant_exists(int lprc, int nv, int wgs);
+
+} // namespace rn

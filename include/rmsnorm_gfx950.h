@@ -1,0 +1,209 @@
+/*
+ * rmsnorm_gfx950.h -- C ABI of the MI355X (gfx950) RMSNorm library.
+ *
+ * Three operations, each one or two HIP kernels enqueued on the caller's stream:
+ *   rmsnorm_fwd                   y = x * rstd * w, plus the fp32 rstd per row
+ *   rmsnorm_bwd                   dx and the fp32 weight gradient dw in one pass
+ *                                 over the rows (deterministic or atomic dw)
+ *   add_rmsnorm_fp8_block_quant   residual add + RMSNorm + e4m3 1x128 block quant
+ *
+ * Conventions shared by every entry point
+ *   - Every function is extern "C", never throws, never allocates device or
+ *     host memory, never synchronizes the device and keeps no per-call state.
+ *     The only global state is a once-per-device cache of device properties.
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     reads inputs and writes outputs only between enqueue and completion of
+ *     its kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream).  Results are visible to later work on that stream.
+ *   - Matrices are row-major [T, H] with a row stride `ld*` counted in
+ *     ELEMENTS (>= H).  Columns are contiguous.  Every matrix base pointer and
+ *     row stride must be a multiple of 16 bytes, so each row splits into
+ *     16-byte vectors; w must be 16-byte aligned, rstd, dw and block_scale
+ *     4-byte aligned.  Buffers are compared by their byte extents: an output
+ *     whose extent overlaps another buffer's is rejected (RN_ERR_ALIAS).
+ *   - dtype codes: RN_F32 (IEEE binary32) or RN_BF16 (bfloat16, stored as
+ *     its 16-bit pattern).  (x, w) pairs accepted: (f32, f32), (bf16, bf16),
+ *     (bf16, f32).  dy and dx always share x's dtype; rstd and dw are fp32.
+ *   - T >= 0; T == 0 returns RN_OK and enqueues nothing (except that
+ *     rmsnorm_bwd then sets dw to zero, the empty sum).  H >= 1, a multiple
+ *     of 8 for bf16 rows and of 4 for f32 rows, and at most
+ *       rmsnorm_fwd                  32768 (bf16 rows), 16384 (f32 rows)
+ *       rmsnorm_bwd                  16384 (bf16 rows),  8192 (f32 rows)
+ *       add_rmsnorm_fp8_block_quant  32768, a multiple of 128
+ *     (RN_ERR_SHAPE beyond).
+ *   - On any error the function returns a non-zero rn_status, enqueues
+ *     nothing and touches no output.  Argument checks happen before any HIP
+ *     call; a failed launch is reported as RN_ERR_LAUNCH.
+ *   - Thread-safe.  Calls on one stream execute in order; calls on different
+ *     streams that write the same buffers race (as any two kernels would).
+ *
+ * Sources of the operations (pages on the subject; titles and sections):
+ *   [C] FlashInfer commit #5741 "cake_rmsnorm_train", quoted on the FlashInfer
+ *       PR #4480 page: Summary; Design (Forward, Backward); API; Memory;
+ *       Determinism.
+ *   [F] FlashInfer PR #4480 "Add FusedAddRMSNormFP8BlockQuant": description
+ *       (Kernel, API) and review thread (scale layout, e4m3 only, strides).
+ *   [L] Liger-Kernel PR #1336 "perf(cutedsl): fused dX+dW backward +
+ *       host-enqueue caching for RMSNorm": the fused single-pass dX+dW
+ *       strip-reduction backward.
+ *   [M] miles-ext-kernels PR #15 (re-vendoring the Cake RMSNorm packages):
+ *       Summary and Accuracy, the per-element dw budget against an FP64 sum.
+ */
+#ifndef RMSNORM_GFX950_H
+#define RMSNORM_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RN_OK = 0,
+    RN_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    RN_ERR_SHAPE = 2,       /* T < 0, H out of range or not a vector multiple    */
+    RN_ERR_DTYPE = 3,       /* unknown dtype code or unsupported (x, w) pair     */
+    RN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
+    RN_ERR_STRIDE = 5,      /* a row stride < H, or not a 16-byte multiple       */
+    RN_ERR_WORKSPACE = 6,   /* deterministic backward: workspace missing/short   */
+    RN_ERR_ALIAS = 7,       /* an output overlaps an input or another output     */
+    RN_ERR_DEVICE = 8,      /* no current HIP device, or it is not gfx950        */
+    RN_ERR_LAUNCH = 9       /* the kernel launch failed (hipGetLastError)        */
+} rn_status;
+
+typedef enum { RN_F32 = 0, RN_BF16 = 1 } rn_dtype;
+
+#define RN_MAX_H 32768
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* rn_status_string(int status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int rn_version(void);
+
+/*
+ * RMSNorm forward  ([C] Summary and Design: Forward).
+ *   rstd[r] = 1 / sqrt( (sum_j x[r,j]^2) / H + eps )        (fp32)
+ *   y[r,j]  = round_dtype( x[r,j] * rstd[r] * w[j] )
+ * The sum of squares and every product are fp32; the square root and the
+ * divisions are IEEE (correctly rounded); y is rounded to x's dtype with
+ * round-to-nearest-even.  rstd is what rmsnorm_bwd expects as its input.
+ *   x     [T, ldx]  x_dtype        input
+ *   w     [H]       w_dtype        input
+ *   y     [T, ldy]  x_dtype        output (may not overlap x)
+ *   rstd  [T]       fp32           output
+ */
+int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype,
+                const void* w, int w_dtype,
+                void* y, int64_t ldy, float* rstd,
+                int64_t T, int64_t H, float eps, void* stream);
+
+/*
+ * Size in bytes of the workspace that a deterministic rmsnorm_bwd needs for
+ * (T, H) on HIP device `device` (fp32 partial sums, one row of H per row
+ * chunk).  The value never decreases with T, so a workspace sized for the
+ * largest T can be reused for every smaller T.  Returns 0 for T == 0 and
+ * (size_t)-1 on invalid arguments or when the device cannot be queried.
+ */
+size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t H, int device);
+
+/*
+ * RMSNorm backward: dx and dw in one pass over the rows
+ * ([C] Design: Backward and Determinism; [L] fused dX+dW backward).
+ *   xhat    = x * rstd
+ *   c[r]    = (1/H) * sum_j dy[r,j] * w[j] * xhat[r,j]
+ *   dx[r,j] = round_dtype( rstd[r] * (dy[r,j] * w[j] - c[r] * xhat[r,j]) )
+ *   dw[j]   = sum_r dy[r,j] * x[r,j] * rstd[r]                (fp32 result)
+ * rstd is the forward's stored fp32 value.  dw is OVERWRITTEN.  Each row
+ * chunk's dw partial is accumulated per column in FP64 from exact products
+ * and rounded once to fp32; the chunk partials are then summed per column in
+ * FP64 and rounded once more.
+ *   deterministic != 0: the partials go to `workspace` and a second kernel
+ *     sums them in a fixed order, so dw is bitwise identical from call to call
+ *     (the order depends only on T, H and the device's CU count).  Needs
+ *     workspace_bytes >= rmsnorm_bwd_workspace_bytes(T, H, device), else
+ *     RN_ERR_WORKSPACE; the workspace content on entry does not matter.
+ *   deterministic == 0: dw is zeroed on the stream and the partials are added
+ *     with fp32 atomics (order not fixed); workspace may be NULL.
+ *   dy [T, lddy] x_dtype; x [T, ldx] x_dtype; w [H] w_dtype; rstd [T] fp32
+ *   dx [T, lddx] x_dtype output; dw [H] fp32 output.
+ */
+int rmsnorm_bwd(const void* dy, int64_t lddy,
+                const void* x, int64_t ldx, int x_dtype,
+                const void* w, int w_dtype,
+                const float* rstd,
+                void* dx, int64_t lddx, float* dw,
+                int64_t T, int64_t H, int deterministic,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused residual add + RMSNorm + FP8 e4m3 1x128 block quant
+ * ([F] description: Kernel and API; review thread on the scale layout).
+ * bf16 only; H a multiple of 128.  Per row r:
+ *   h[r,j]      = bf16( x[r,j] + residual[r,j] )     written back to residual
+ *   rstd        = 1 / sqrt( (sum_j h[r,j]^2) / H + eps )   (fp32, not stored)
+ *   n[r,j]      = bf16( h[r,j] * rstd * w[j] )        written to normed_out
+ *   per block k (columns 128k .. 128k+127):
+ *     a         = max_j |n[r,j]|                      (exact)
+ *     s         = a / 448.0f                          (IEEE fp32 division)
+ *     block_scale[k * scale_ld + r] = s
+ *     out[r,j]  = e4m3fn( n[r,j] / s )   IEEE fp32 quotient, rounded to
+ *                 nearest even onto E4M3FN, saturating at +-448, sign kept;
+ *                 an all-zero block has s = 0 and codes 0x00.
+ * The codes are therefore exactly a re-quantisation of normed_out.
+ *   x           [T, ldx]  bf16   input
+ *   residual    [T, ldr]  bf16   input and output (in place; the only
+ *                                buffer that may be both)
+ *   w           [H]       bf16   input
+ *   out         [T, ldo]  uint8  e4m3fn codes, output (ldo in bytes, %16 == 0)
+ *   block_scale [H/128, scale_ld] fp32 output, row index fastest
+ *               (column-major (H/128, round_up(T,4)) when scale_ld is
+ *               round_up(T,4)); scale_ld >= T and scale_ld % 4 == 0; entries
+ *               for rows T .. scale_ld-1 are not written.
+ *   normed_out  [T, ldn]  bf16   output
+ */
+int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx,
+                                void* residual, int64_t ldr,
+                                const void* w,
+                                uint8_t* out, int64_t ldo,
+                                float* block_scale, int64_t scale_ld,
+                                void* normed_out, int64_t ldn,
+                                int64_t T, int64_t H, float eps, void* stream);
+
+/*
+ * Host-only launch policy query (no HIP call; usable without a GPU).
+ * op: 0 = forward, 1 = backward, 2 = fused fp8 producer.
+ * Fills out[0..5] = { lanes per row, 16-byte vectors per lane, threads per
+ * work-group, work-groups (row chunks), rows per work-group pass, kernel id }
+ * for a device with `cu_count` compute units.  Returns an rn_status.
+ */
+int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype,
+                    int cu_count, int32_t* out);
+
+/* Workspace bytes for a device with `cu_count` CUs (host-only twin of
+ * rmsnorm_bwd_workspace_bytes). */
+size_t rn_bwd_workspace_bytes_for(int64_t T, int64_t H, int cu_count);
+
+/*
+ * Self-test hooks for the fp8 producer's quantisation step (diagnostics; the
+ * test suite calls them on a GPU).
+ * rn_selftest_quant: for every bf16 block maximum a with bit pattern in
+ *   [a_lo, a_hi] (1 .. 0x7f7f) and every bf16 n with |n| <= a (both signs),
+ *   compares the codes the producer kernel computes for n with scale
+ *   s = a/448 against e4m3(n / s) with the IEEE fp32 division; adds the
+ *   number of mismatching 8-value chunks to *d_mismatches and lowers
+ *   *d_first_bad to (a << 16 | n-magnitude) of the first failure.  Both are
+ *   device pointers the caller initialises.  Returns 0, 2 (bad range) or 9.
+ * rn_selftest_cvt_e4m3: d_out[i] = e4m3 code of fp32 d_in[i] (i < n), made by
+ *   the same conversion instruction the producer uses.  Returns 0, 1 or 9.
+ */
+int rn_selftest_quant(uint32_t a_lo, uint32_t a_hi, unsigned long long* d_mismatches,
+                      uint32_t* d_first_bad, void* stream);
+int rn_selftest_cvt_e4m3(const float* d_in, uint8_t* d_out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_GFX950_H */

@@ -1,0 +1,201 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+* the shared library loads and exports every function declared in
+  include/rmsnorm_gfx950.h;
+* status strings, version;
+* the launch policy (a pure host function) for the workload shapes;
+* argument validation: each call below carries an argument error that the
+  library must reject before it touches the device, so no pointer passed here
+  is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm_gfx950.h")
+
+
+@pytest.fixture(scope="module")
+def rn():
+    lib_path = os.path.join(ROOT, "bwd_fp8_block_amd", "librmsnorm_gfx950.so")
+    if not os.path.exists(lib_path):
+        from bwd_fp8_block_amd import build as b
+        b.build()
+    import bwd_fp8_block_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(rn):
+    names = declared_functions()
+    assert {"rmsnorm_fwd", "rmsnorm_bwd", "add_rmsnorm_fp8_block_quant", "rmsnorm_bwd_workspace_bytes"} <= set(names)
+    lib = ctypes.CDLL(rn.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(rn):
+    for code, text in [(0, "ok"), (1, "null pointer"), (2, "unsupported shape"), (3, "unsupported dtype"),
+                       (4, "misaligned pointer"), (5, "bad row stride"), (6, "workspace missing or too small"),
+                       (7, "overlapping buffers"), (8, "no gfx950 device"), (9, "kernel launch failed")]:
+        assert rn.rn_status_string(code) == text
+    assert rn.rn_status_string(99) == "unknown status"
+    assert rn.rn_version() >= 10000
+
+
+CU = 256
+
+
+@pytest.mark.parametrize("op,T,H,xd,wd", [
+    (0, 64, 256, 0, 0), (1, 64, 256, 0, 0),
+    (0, 8192, 4096, 1, 1), (1, 8192, 4096, 1, 1),
+    (1, 58497, 2048, 1, 0), (0, 65536, 5120, 1, 0), (1, 65536, 5120, 1, 0),
+    (2, 4096, 7168, 1, 1), (2, 8192, 4096, 1, 1), (2, 3, 1152, 1, 1), (2, 1, 128, 1, 1),
+    (0, 5, 8, 1, 1), (1, 5, 8, 1, 1), (0, 100, 32768, 1, 1), (1, 9, 16384, 1, 1), (2, 9, 32768, 1, 1),
+])
+def test_policy_invariants(rn, op, T, H, xd, wd):
+    p = rn.rn_query_policy(op, T, H, xd, wd, CU)
+    E = 8 if xd == 1 else 4
+    nch = H // E
+    assert p["lpr"] in (16, 32) or p["lpr"] % 64 == 0
+    assert p["lpr"] * p["nv"] >= nch                         # every chunk owned by a lane
+    assert p["lpr"] * (p["nv"] - 1) < nch                    # no fully idle vector slot
+    assert p["wgs"] % p["lpr"] == 0 and p["wgs"] <= 1024 and p["gpw"] == p["wgs"] // p["lpr"]
+    assert 1 <= p["grid"] <= max(1, -(-T // p["gpw"]))       # no work-group without rows
+    if op == 2:
+        assert p["lpr"] % 16 == 0                            # 1x128 block = 16 lanes
+    if op == 1:
+        assert p["grid"] <= CU                               # one row strip per CU at most
+
+
+def test_policy_shapes_of_the_workloads(rn):
+    assert rn.rn_query_policy(0, 8192, 4096, 1, 1, CU)["lpr"] == 64                 # one row per wavefront
+    b = rn.rn_query_policy(1, 8192, 4096, 1, 1, CU)
+    assert b["nv"] == 1 and b["lpr"] == 512 and b["grid"] == 256
+    f = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
+    assert f["lpr"] == 128 and f["nv"] == 7
+
+
+def test_policy_rejects_out_of_range(rn):
+    with pytest.raises(rn.RNError):
+        rn.rn_query_policy(0, 10, 65536, 1, 1, CU)
+    with pytest.raises(rn.RNError):
+        rn.rn_query_policy(1, 10, 32768, 1, 1, CU)          # bwd bf16 rows up to 16384
+    with pytest.raises(rn.RNError):
+        rn.rn_query_policy(2, 10, 1000, 1, 1, CU)           # fp8 needs H % 128 == 0
+    with pytest.raises(rn.RNError):
+        rn.rn_query_policy(2, 10, 1024, 0, 0, CU)           # fp8 is bf16-only
+    with pytest.raises(rn.RNError):
+        rn.rn_query_policy(0, 10, 1024, 0, 1, CU)           # (f32 x, bf16 w) not a valid pair
+
+
+def test_workspace_bytes_monotone_and_reusable(rn):
+    assert rn.rn_bwd_workspace_bytes_for(0, 4096, CU) == 0
+    prev = 0
+    for T in (1, 2, 3, 7, 64, 255, 1000, 8192, 58497, 65536, 10 ** 6):
+        b = rn.rn_bwd_workspace_bytes_for(T, 4096, CU)
+        assert b >= prev and b % 256 == 0
+        prev = b
+    assert rn.rn_bwd_workspace_bytes_for(8192, 4096, CU) == 256 * 4096 * 4
+    with pytest.raises(rn.RNError):
+        rn.rn_bwd_workspace_bytes_for(10, 4097, CU)
+
+
+# --- validation-only calls: every one carries an error caught before any device work.
+# The pointers are fake, so these run only where no GPU is visible: on a GPU
+# machine the same paths are exercised with real buffers in test_parity_gpu.py.
+no_gpu = pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                            reason="fake-pointer validation tests run only without a GPU")
+A = 0x10000          # a 16-byte aligned address that is never dereferenced
+B = 0x20000000
+C = 0x40000000
+
+
+@no_gpu
+def test_fwd_validation(rn):
+    lib = rn.lib
+    f = lib.rmsnorm_fwd
+    # bad dtype pair
+    assert f(A, 256, 0, B, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 3
+    assert f(A, 256, 7, B, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 3
+    # H not a multiple of the vector width / out of range
+    assert f(A, 256, 1, B, 1, C, 256, C + 4096, 4, 250, 1e-6, None) == 2
+    assert f(A, 40000, 1, B, 1, C, 40000, C + 4096, 4, 40000, 1e-6, None) == 2
+    assert f(A, 256, 1, B, 1, C, 256, C + 4096, -1, 256, 1e-6, None) == 2
+    # T == 0: nothing to do, nothing touched (null pointers allowed)
+    assert f(None, 256, 1, None, 1, None, 256, None, 0, 256, 1e-6, None) == 0
+    # null pointers
+    assert f(None, 256, 1, B, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 1
+    assert f(A, 256, 1, B, 1, C, 256, None, 4, 256, 1e-6, None) == 1
+    # misaligned
+    assert f(A + 2, 256, 1, B, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 4
+    assert f(A, 256, 1, B + 8, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 4
+    assert f(A, 256, 1, B, 1, C, 256, C + 4098, 4, 256, 1e-6, None) == 4
+    # strides
+    assert f(A, 255, 1, B, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 5
+    assert f(A, 260, 1, B, 1, C, 256, C + 4096, 4, 256, 1e-6, None) == 5      # 520 B, not 16-B multiple
+    # aliasing: y overlaps x; rstd inside y
+    assert f(A, 256, 1, B, 1, A + 512, 256, C, 4, 256, 1e-6, None) == 7
+    assert f(A, 256, 1, B, 1, C, 256, C + 16, 4, 256, 1e-6, None) == 7
+
+
+@no_gpu
+def test_bwd_validation(rn):
+    f = rn.lib.rmsnorm_bwd
+    args = dict(dy=A, lddy=256, x=A + 0x100000, ldx=256, xd=1, w=B, wd=1, rstd=B + 0x1000,
+                dx=C, lddx=256, dw=C + 0x100000, T=4, H=256, det=1, ws=C + 0x200000, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["dy"], a["lddy"], a["x"], a["ldx"], a["xd"], a["w"], a["wd"], a["rstd"], a["dx"],
+                 a["lddx"], a["dw"], a["T"], a["H"], a["det"], a["ws"], a["wsb"], None)
+
+    assert call(xd=0, wd=1) == 3
+    assert call(H=252) == 2
+    assert call(H=16392) == 2                      # beyond the backward's range for bf16 rows
+    assert call(dw=None) == 1
+    assert call(dy=None) == 1
+    assert call(dw=C + 0x100002) == 4
+    assert call(x=A + 0x100008) == 4
+    assert call(lddx=100) == 5
+    assert call(dx=A + 64) == 7                    # dx overlaps dy
+    assert call(dw=A + 64) == 7                    # dw inside dy
+    assert call(ws=None) == 6                      # deterministic without a workspace
+    assert call(ws=C + 0x200008) == 4
+
+
+@no_gpu
+def test_fp8_validation(rn):
+    f = rn.lib.add_rmsnorm_fp8_block_quant
+    args = dict(x=A, ldx=256, r=A + 0x100000, ldr=256, w=B, out=C, ldo=256, sc=C + 0x100000, sld=8,
+                n=C + 0x200000, ldn=256, T=4, H=256)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["x"], a["ldx"], a["r"], a["ldr"], a["w"], a["out"], a["ldo"], a["sc"], a["sld"], a["n"],
+                 a["ldn"], a["T"], a["H"], 1e-6, None)
+
+    assert call(H=200) == 2                        # not a multiple of 128
+    assert call(H=1000) == 2
+    assert call(T=-1) == 2
+    assert call(T=0, x=None, r=None, w=None, out=None, sc=None, n=None) == 0
+    assert call(out=None) == 1
+    assert call(out=C + 8) == 4
+    assert call(sc=C + 0x100002) == 4
+    assert call(ldo=200) == 5
+    assert call(sld=3) == 5                        # scale_ld < T
+    assert call(sld=6) == 5                        # scale_ld % 4 != 0
+    assert call(n=A + 16) == 7                     # normed overlaps x
+    assert call(sc=C + 64) == 7                    # scales inside out
+    assert call(r=A) == 7                          # residual is x

@@ -1,0 +1,393 @@
+"""Parity of the HIP path (through the C ABI) with the FP64 CPU oracle.
+
+Small and ragged shapes are compared element by element; the five workload
+configurations are run at full size in the launch configuration the benchmark
+times, with sampled rows (and the full dw / rstd / fp8 outputs) checked against
+the oracle.  Every output buffer is surrounded by guard bands that must come
+back untouched."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (as_f64, check_dw, check_rstd, check_values, sample_rows, to_dev, to_host,
+                        torch_dtype)
+from workloads import CONFIGS, Workload, generate
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_BF16 = 0x7FBF      # a NaN pattern no kernel writes
+SENTINEL_F32 = np.float32(np.nan)
+
+
+@pytest.fixture(scope="module")
+def rn():
+    import bwd_fp8_block_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def guarded_matrix(T, H, dtype, ld=None, guard=64):
+    """A [T, ld] buffer plus guard elements on both sides, filled with a sentinel.
+    Returns (full flat tensor, [T, H] view with row stride ld)."""
+    ld = ld or H
+    n = guard + T * ld + guard
+    if dtype == torch.bfloat16:
+        full = torch.full((n,), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    elif dtype == torch.uint8:
+        full = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    else:
+        full = torch.full((n,), float("nan"), dtype=dtype, device="cuda")
+    view = full[guard: guard + T * ld].view(T, ld)[:, :H] if T > 0 else full[guard:guard].view(0, H)
+    return full, view
+
+
+def assert_guards(full: torch.Tensor, T, H, ld, guard=64, name="out"):
+    h = to_host(full)
+    if full.dtype == torch.bfloat16:
+        sent = lambda a: a == SENTINEL_BF16
+    elif full.dtype == torch.uint8:
+        sent = lambda a: a == 0xA5
+    else:
+        sent = lambda a: np.isnan(a)
+    assert sent(h[:guard]).all() and sent(h[guard + T * ld:]).all(), "%s: guard band overwritten" % name
+    if ld > H and T > 0:
+        body = h[guard: guard + T * ld].reshape(T, ld)
+        assert sent(body[:, H:]).all(), "%s: row padding overwritten" % name
+
+
+def gpu_fwd(rn, x: np.ndarray, w: np.ndarray, eps: float, ld_pad=0):
+    T, H = x.shape
+    xd, wd = to_dev(x), to_dev(w)
+    ld = H + ld_pad
+    yfull, y = guarded_matrix(T, H, torch_dtype(x), ld)
+    rfull, rstd = guarded_matrix(1, T, torch.float32)
+    rstd = rstd.view(T)
+    rn.rmsnorm_fwd(xd, wd, y, rstd, eps)
+    torch.cuda.synchronize()
+    assert_guards(yfull, T, H, ld, name="y")
+    assert_guards(rfull, 1, T, T, name="rstd")
+    return to_host(y) if T else np.zeros((0, H), x.dtype), to_host(rstd)
+
+
+def gpu_bwd(rn, dy, x, w, rstd, det, ld_pad=0, poison=False):
+    T, H = x.shape
+    dyd, xd, wd = to_dev(dy), to_dev(x), to_dev(w)
+    rd = torch.from_numpy(np.ascontiguousarray(rstd, dtype=np.float32)).cuda()
+    ld = H + ld_pad
+    dxfull, dx = guarded_matrix(T, H, torch_dtype(x), ld)
+    dwfull, dw = guarded_matrix(1, H, torch.float32)
+    dw = dw.view(H)
+    ws = None
+    if det:
+        nbytes = rn.rmsnorm_bwd_workspace_bytes(T, H)
+        ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda")
+        if poison:
+            ws.fill_(float("nan"))
+    rn.rmsnorm_bwd(dyd, xd, wd, rd, dx, dw, deterministic=det, workspace=ws)
+    torch.cuda.synchronize()
+    assert_guards(dxfull, T, H, ld, name="dx")
+    assert_guards(dwfull, 1, H, H, name="dw")
+    return to_host(dx) if T else np.zeros((0, H), x.dtype), to_host(dw)
+
+
+# ----------------------------------------------------------------------------
+# fp8 conversion and quotient self-tests (exhaustive over the reachable inputs)
+# ----------------------------------------------------------------------------
+def test_quant_step_exhaustive(rn):
+    """For every bf16 block maximum a and every bf16 n with |n| <= a, the kernel's
+    quotient-and-round gives the codes of e4m3(n / (a/448)) with IEEE division."""
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    for lo, hi in ((0x0001, 0x3FFF), (0x4000, 0x5FFF), (0x6000, 0x7F7F)):
+        rn.rn_selftest_quant(lo, hi, mism, first)
+        torch.cuda.synchronize()
+    assert int(mism.item()) == 0, "first mismatch at 0x%08x" % (int(first.item()) & 0xFFFFFFFF)
+
+
+def test_cvt_e4m3_matches_oracle_encoder(rn, oracle):
+    """The producer's conversion instruction against the oracle's E4M3FN encoder at every
+    rounding boundary (midpoints between codes and their fp32 neighbours, both signs),
+    near the top of the range, and on random values; |v| < 464 (quotients never exceed
+    448 * (1 + 2^-22))."""
+    mags = sorted({abs(oracle.e4m3_to_double(c)) for c in range(0x7F)})
+    pts = []
+    for lo, hi in zip(mags[:-1], mags[1:]):
+        m = np.float32((lo + hi) / 2)
+        pts += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9)), np.float32(lo)]
+    pts += [np.float32(448.0) * np.float32(1 + k * 2.0 ** -23) for k in range(16)]
+    pts += [np.float32(2.0 ** -10), np.float32(0.0), np.float32(1e-30), np.float32(460.0)]
+    rng = np.random.default_rng(30)
+    rnd = (rng.uniform(-1, 1, 200000) * np.exp2(rng.integers(-14, 9, 200000))).astype(np.float32)
+    v = np.concatenate([np.array(pts, np.float32), -np.array(pts, np.float32), rnd])
+    v = v[np.abs(v) < 464]
+    out = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+    rn.rn_selftest_cvt_e4m3(torch.from_numpy(v).cuda(), out)
+    got = to_host(out)
+    ref = np.array([oracle.float_to_e4m3(x) for x in v], np.uint8)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, "first mismatch: value %r gpu 0x%02x oracle 0x%02x" % (v[bad[0]], got[bad[0]], ref[bad[0]])
+
+
+# ----------------------------------------------------------------------------
+# forward
+# ----------------------------------------------------------------------------
+FWD_CASES = [
+    # T, H, x dtype, w dtype, row padding (elements)
+    (64, 256, "f32", "f32", 0), (1, 8, "bf16", "bf16", 0), (2, 16, "f32", "f32", 4), (7, 120, "bf16", "bf16", 8),
+    (63, 512, "bf16", "f32", 0), (65, 1000, "bf16", "bf16", 64), (127, 1024, "f32", "f32", 0),
+    (129, 2048, "bf16", "f32", 0), (257, 4096, "bf16", "bf16", 4096), (33, 5120, "bf16", "f32", 0),
+    (17, 7168, "bf16", "bf16", 0), (9, 8200, "bf16", "bf16", 0), (5, 12288, "bf16", "bf16", 0),
+    (3, 32768, "bf16", "bf16", 0), (3, 16384, "f32", "f32", 0), (1000, 128, "bf16", "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("T,H,xd,wd,pad", FWD_CASES)
+def test_fwd_parity(rn, oracle, T, H, xd, wd, pad):
+    x = generate(Workload("fwd", T, H, xd, wd, seed=1000 + T + H))
+    y, rstd = gpu_fwd(rn, x["x"], x["w"], 1e-6, ld_pad=pad)
+    yref, rref = oracle.rmsnorm_fwd(x["x"], x["w"], 1e-6)
+    check_rstd(rstd, rref)
+    check_values("y", y, yref, xd == "bf16")
+
+
+def test_fwd_edge_rows(rn, oracle):
+    """All-zero rows, constant rows, tiny and huge scales, one extreme row."""
+    T, H = 12, 1024
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 3.0
+    x[2] = -0.5
+    x[3] *= 1e-3
+    x[4] *= 1e3
+    x[5, 7] = 3e4                       # one extreme element
+    x[6] *= 1e-20                       # below eps: rstd ~ 1/sqrt(eps)
+    from workloads import to_bf16_bits
+    xb = to_bf16_bits(x)
+    w = to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    y, rstd = gpu_fwd(rn, xb, w, 1e-6)
+    yref, rref = oracle.rmsnorm_fwd(xb, w, 1e-6)
+    check_rstd(rstd, rref)
+    check_values("y", y, yref, True)
+    assert np.all(as_f64(y[0]) == 0.0)
+    np.testing.assert_allclose(as_f64(y[1]), as_f64(w), rtol=2 ** -7)     # constant row -> w
+
+
+def test_fwd_empty(rn):
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    rn.rmsnorm_fwd(x, torch.ones(256, dtype=torch.bfloat16, device="cuda"), torch.empty_like(x),
+                   torch.empty(0, dtype=torch.float32, device="cuda"), 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+BWD_CASES = [
+    (64, 256, "f32", "f32", 0), (1, 8, "bf16", "bf16", 0), (3, 64, "f32", "f32", 4), (7, 120, "bf16", "bf16", 8),
+    (63, 512, "bf16", "f32", 0), (65, 1000, "bf16", "bf16", 64), (127, 1024, "f32", "f32", 0),
+    (129, 2048, "bf16", "f32", 0), (257, 4096, "bf16", "bf16", 0), (300, 5120, "bf16", "f32", 16),
+    (31, 7168, "bf16", "bf16", 0), (9, 8200, "bf16", "bf16", 0), (5, 16384, "bf16", "bf16", 0),
+    (4, 8192, "f32", "f32", 0), (2000, 256, "bf16", "bf16", 0), (1100, 128, "f32", "f32", 0),
+]
+
+
+@pytest.mark.parametrize("det", [True, False], ids=["det", "atomic"])
+@pytest.mark.parametrize("T,H,xd,wd,pad", BWD_CASES)
+def test_bwd_parity(rn, oracle, T, H, xd, wd, pad, det):
+    d = generate(Workload("bwd", T, H, xd, wd, seed=2000 + T + H))
+    _, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6)
+    dx, dw = gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, det, ld_pad=pad)
+    dxref, dwref = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float64))
+    check_values("dx", dx, dxref, xd == "bf16")
+    check_dw(dw, dwref)
+
+
+def test_bwd_empty_sets_dw_zero(rn):
+    H = 512
+    dw = torch.full((H,), 7.0, device="cuda")
+    e = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+    rn.rmsnorm_bwd(e, e.clone(), torch.ones(H, dtype=torch.bfloat16, device="cuda"),
+                   torch.empty(0, device="cuda"), e.clone(), dw, deterministic=True, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+
+
+def test_bwd_det_bitwise_repeatable_with_poisoned_workspace(rn):
+    d = generate(Workload("det", 3001, 2048, "bf16", "f32", seed=77))
+    _, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6)
+    outs = [gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, True, poison=True) for _ in range(3)]
+    for dx, dw in outs[1:]:
+        assert np.array_equal(dw.view(np.uint32), outs[0][1].view(np.uint32))
+        assert np.array_equal(dx, outs[0][0])
+
+
+# ----------------------------------------------------------------------------
+# fused residual add + RMSNorm + fp8 block quant
+# ----------------------------------------------------------------------------
+def gpu_fp8(rn, x, res, w, eps, ld_pad=0, scale_pad=0):
+    T, H = x.shape
+    ld = H + ld_pad
+    xd, wd = to_dev(x), to_dev(w)
+    rfull, r = guarded_matrix(T, H, torch.bfloat16, ld)
+    if T:
+        r.copy_(to_dev(res))
+    ofull, o = guarded_matrix(T, H, torch.uint8, ld)
+    nfull, n = guarded_matrix(T, H, torch.bfloat16, ld)
+    sld = (T + 3) // 4 * 4 + scale_pad
+    sfull, s = guarded_matrix(H // 128, sld, torch.float32)
+    rn.add_rmsnorm_fp8_block_quant(xd, r, wd, o, s, n, eps)
+    torch.cuda.synchronize()
+    assert_guards(rfull, T, H, ld, name="residual")
+    assert_guards(ofull, T, H, ld, name="out")
+    assert_guards(nfull, T, H, ld, name="normed")
+    sh = to_host(s)
+    assert np.all(np.isnan(sh[:, T:])), "scale padding rows were written"
+    assert_guards(sfull, H // 128, sld, sld, name="block_scale")
+    return to_host(r), to_host(o), sh, to_host(n)
+
+
+def check_fp8(oracle, x, res, w, eps, h, out, scale, normed):
+    T = x.shape[0]
+    ref = oracle.add_rmsnorm_fp8(x, res, w, eps)
+    assert np.array_equal(h, ref["h"]), "residual not bit-exact"
+    check_values("normed", normed, ref["normed"], True)
+    sref, cref = oracle.block_quant_e4m3(normed, scale_ld=scale.shape[1])
+    assert np.array_equal(scale[:, :T].view(np.uint32), sref[:, :T].view(np.uint32)), "block scales not bit-exact"
+    bad = np.argwhere(out != cref)
+    assert bad.size == 0, "fp8 codes differ at %s (gpu 0x%02x, oracle 0x%02x)" % (
+        bad[0], out[tuple(bad[0])], cref[tuple(bad[0])])
+    # the oracle's own end-to-end codes: equal wherever its bf16 normed equals the GPU's
+    same = ref["normed_bf16"] == normed
+    assert np.array_equal(ref["codes"][same & np.repeat(
+        (ref["scale"][:, :T].T == scale[:, :T].T), 128, axis=1)], out[same & np.repeat(
+            (ref["scale"][:, :T].T == scale[:, :T].T), 128, axis=1)])
+    return float(same.mean())
+
+
+FP8_CASES = [(1, 128, 0), (3, 256, 16), (5, 384, 0), (64, 1152, 0), (129, 2048, 128), (7, 4096, 0),
+             (33, 7168, 0), (6, 8192, 0), (3, 16384, 0), (2, 32768, 0), (300, 1024, 0)]
+
+
+@pytest.mark.parametrize("T,H,pad", FP8_CASES)
+def test_fp8_parity(rn, oracle, T, H, pad):
+    d = generate(Workload("fp8", T, H, "bf16", "bf16", residual=True, seed=3000 + T + H))
+    h, out, scale, normed = gpu_fp8(rn, d["x"], d["residual"], d["w"], 1e-6, ld_pad=pad, scale_pad=4)
+    check_fp8(oracle, d["x"], d["residual"], d["w"], 1e-6, h, out, scale, normed)
+
+
+def test_fp8_edge_rows(rn, oracle):
+    """A row whose sum cancels to zero (scale 0, codes 0), tiny and huge rows, a
+    block of zeros inside a row, signed zeros."""
+    from workloads import to_bf16_bits
+    T, H = 8, 1024
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    xb, rb = to_bf16_bits(x), to_bf16_bits(r)
+    rb[0] = xb[0] ^ 0x8000                           # x + r == 0 exactly
+    xb[1] = to_bf16_bits(x[1] * 1e-3)
+    rb[1] = to_bf16_bits(r[1] * 1e-3)
+    xb[2] = to_bf16_bits(x[2] * 1e3)
+    xb[3, 128:256] = 0
+    rb[3, 128:256] = 0x8000                          # a zero block (mixed signed zeros)
+    xb[4] = to_bf16_bits(x[4] * 1e-30)
+    rb[4] = 0
+    w = to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    h, out, scale, normed = gpu_fp8(rn, xb, rb, w, 1e-6)
+    check_fp8(oracle, xb, rb, w, 1e-6, h, out, scale, normed)
+    assert np.all(scale[:, 0] == 0) and np.all(out[0] == 0)
+    assert scale[1, 3] == 0 and np.all(out[3, 128:256] == 0)
+
+
+# ----------------------------------------------------------------------------
+# the workload configurations at full size
+# ----------------------------------------------------------------------------
+_cache = {}
+
+
+def workload(name):
+    if name not in _cache:
+        _cache.clear()
+        _cache[name] = generate(CONFIGS[name])
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", ["c1_f32_T64_H256", "c2_bf16_T8192_H4096", "c3_bf16_T58497_H2048_outliers",
+                                  "c5_bf16_T65536_H5120"])
+def test_config_fwd_bwd(rn, oracle, name):
+    wl = CONFIGS[name]
+    d = workload(name)
+    T, H = wl.T, wl.H
+    bf = wl.x_dtype == "bf16"
+    xd, wd, dyd = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+    y = torch.empty_like(xd)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd(xd, wd, y, rstd, wl.eps)
+    rstd_h = to_host(rstd)
+    _, rref = oracle.rmsnorm_fwd(d["x"], d["w"], wl.eps, want_y=False)
+    check_rstd(rstd_h, rref)
+    rows = sample_rows(T)
+    yh = to_host(y[torch.from_numpy(rows).cuda()])
+    yref, _ = oracle.rmsnorm_fwd(np.ascontiguousarray(d["x"][rows]), d["w"], wl.eps)
+    check_values("y", yh, yref, bf)
+    del y
+
+    dx = torch.empty_like(xd)
+    dw = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4, dtype=torch.float32, device="cuda")
+    _, dwref = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd_h.astype(np.float64), want_dx=False)
+    dws = []
+    for rep in range(3):
+        ws.fill_(float("nan"))                            # poisoned between runs
+        rn.rmsnorm_bwd(dyd, xd, wd, rstd, dx, dw, deterministic=True, workspace=ws)
+        dws.append(to_host(dw).copy())
+        if rep == 0:
+            check_dw(dws[0], dwref)
+            dxh = to_host(dx[torch.from_numpy(rows).cuda()])
+            dxref, _ = oracle.rmsnorm_bwd(np.ascontiguousarray(d["dy"][rows]), np.ascontiguousarray(d["x"][rows]),
+                                          d["w"], rstd_h[rows].astype(np.float64), want_dw=False)
+            check_values("dx", dxh, dxref, bf)
+    for other in dws[1:]:
+        assert np.array_equal(other.view(np.uint32), dws[0].view(np.uint32)), "deterministic dw changed"
+    rn.rmsnorm_bwd(dyd, xd, wd, rstd, dx, dw, deterministic=False)
+    check_dw(to_host(dw), dwref)
+
+
+@pytest.mark.parametrize("name", ["c4_fp8_T4096_H7168", "fp8_T8192_H4096"])
+def test_config_fp8(rn, oracle, name):
+    wl = CONFIGS[name]
+    d = workload(name)
+    h, out, scale, normed = gpu_fp8(rn, d["x"], d["residual"], d["w"], wl.eps)
+    agree = check_fp8(oracle, d["x"], d["residual"], d["w"], wl.eps, h, out, scale, normed)
+    assert agree > 0.999                                  # bf16 normed differs only at rounding ties
+
+
+# ----------------------------------------------------------------------------
+# validation with real buffers (errors must leave outputs untouched)
+# ----------------------------------------------------------------------------
+def test_validation_with_real_buffers(rn):
+    T, H = 4, 256
+    x = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+    w = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((T, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    rstd = torch.full((T,), 5.0, device="cuda")
+    big = torch.zeros(T * H + 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rn.RNError) as e:                  # misaligned x (offset by one element)
+        rn.rmsnorm_fwd(big[1:1 + T * H].view(T, H), w, y, rstd, 1e-6)
+    assert e.value.status == 4
+    with pytest.raises(rn.RNError) as e:                  # y aliases x
+        rn.rmsnorm_fwd(x, w, x, rstd, 1e-6)
+    assert e.value.status == 7
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0) and torch.all(rstd == 5.0)
+    dx = torch.zeros_like(x)
+    dw = torch.full((H,), 9.0, device="cuda")
+    small = torch.empty(4, device="cuda")
+    with pytest.raises(rn.RNError) as e:
+        rn.rmsnorm_bwd(x, x, w, rstd, dx, dw, deterministic=True, workspace=small)
+    assert e.value.status == 6
+    with pytest.raises(rn.RNError) as e:
+        rn.rmsnorm_bwd(x, x, w, rstd, dx, dw, deterministic=True, workspace=None)
+    assert e.value.status == 6
+    torch.cuda.synchronize()
+    assert torch.all(dw == 9.0) and torch.all(dx == 0)
