@@ -129,6 +129,22 @@ def _stream(dev: torch.device):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+class _NoSwitch:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
+
+
+_NOSWITCH = _NoSwitch()
+
+
+def _on(dev: torch.device):
+    """Make `dev` current for the call (a no-op when it already is)."""
+    return _NOSWITCH if dev.index == torch.cuda.current_device() else torch.cuda.device(dev)
+
+
 def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.Tensor, eps: float) -> None:
     """y = x * rstd * w with rstd = 1/sqrt(mean(x^2) + eps); writes y [T,H] and rstd [T] (fp32)."""
     dev = _dev((x, w, y, rstd))
@@ -137,7 +153,7 @@ def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.T
         raise ValueError("rmsnorm_fwd: shape or dtype mismatch")
     px, ldx = _mat(x, "x")
     py, ldy = _mat(y, "y")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.rmsnorm_fwd(px, ldx, _dt(x), _vec(w, "w"), _dt(w), py, ldy, _vec(rstd, "rstd"),
                              T, H, float(eps), _stream(dev))
     _check("rmsnorm_fwd", st)
@@ -174,7 +190,7 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
         if not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous")
         wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.rmsnorm_bwd(pdy, lddy, px, ldx, _dt(x), _vec(w, "w"), _dt(w), _vec(rstd, "rstd"),
                              pdx, lddx, _vec(dw, "dw"), T, H, 1 if deterministic else 0, wsp, wsb, _stream(dev))
     _check("rmsnorm_bwd", st)
@@ -204,7 +220,7 @@ def add_rmsnorm_fp8_block_quant(x: torch.Tensor, residual: torch.Tensor, w: torc
     pr, ldr = _mat(residual, "residual")
     po, ldo = _mat(out, "out")
     pn, ldn = _mat(normed_out, "normed_out")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.add_rmsnorm_fp8_block_quant(px, ldx, pr, ldr, _vec(w, "w"), po, ldo,
                                              block_scale.data_ptr(), scale_ld, pn, ldn,
                                              T, H, float(eps), _stream(dev))
@@ -213,9 +229,9 @@ def add_rmsnorm_fp8_block_quant(x: torch.Tensor, residual: torch.Tensor, w: torc
 
 def rn_query_policy(op: int, T: int, H: int, x_dtype: int, w_dtype: int, cu_count: int) -> dict:
     """Host-only launch policy (no GPU needed)."""
-    out = (ctypes.c_int32 * 6)()
+    out = (ctypes.c_int32 * 7)()
     _check("rn_query_policy", lib.rn_query_policy(op, T, H, x_dtype, w_dtype, cu_count, out))
-    return dict(lpr=out[0], nv=out[1], wgs=out[2], grid=out[3], gpw=out[4], kernel=out[5])
+    return dict(lpr=out[0], nv=out[1], wgs=out[2], grid=out[3], gpw=out[4], kernel=out[5], flags=out[6])
 
 
 def rn_bwd_workspace_bytes_for(T: int, H: int, cu_count: int) -> int:
@@ -228,7 +244,7 @@ def rn_bwd_workspace_bytes_for(T: int, H: int, cu_count: int) -> int:
 def rn_selftest_quant(a_lo: int, a_hi: int, mismatches: torch.Tensor, first_bad: torch.Tensor) -> None:
     """Exhaustive check of the producer's quantisation step (see the C header)."""
     dev = _dev((mismatches, first_bad))
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.rn_selftest_quant(a_lo, a_hi, mismatches.data_ptr(), first_bad.data_ptr(), _stream(dev))
     _check("rn_selftest_quant", st)
 
@@ -238,6 +254,6 @@ def rn_selftest_cvt_e4m3(x: torch.Tensor, out: torch.Tensor) -> None:
     dev = _dev((x, out))
     if x.dtype != torch.float32 or out.dtype != torch.uint8 or x.numel() != out.numel():
         raise ValueError("rn_selftest_cvt_e4m3: float32 in, uint8 out, same size")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib.rn_selftest_cvt_e4m3(x.data_ptr(), out.data_ptr(), x.numel(), _stream(dev))
     _check("rn_selftest_cvt_e4m3", st)

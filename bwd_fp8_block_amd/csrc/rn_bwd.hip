@@ -32,18 +32,7 @@
 
 namespace rn {
 
-template <int NV>
-__device__ __forceinline__ void bwd_load_row(u32x4 (&v)[NV], const u32x4* row, int lane, int lpr, int nch, bool valid)
-{
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int c = lane + lpr * i;
-        if (valid && c < nch) v[i] = row[c];
-        else v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET, bool NT>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -66,19 +55,23 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     chunk_rows(strip, G, a.T, lo, hi);
     const int n_it = (int)((hi - lo + gpw - 1) / gpw);
 
+    int cix[NV];
+    bool cok[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + lpr * i;
+        cok[i] = c < nch;
+        cix[i] = cok[i] ? c : nch - 1;
+    }
+
     // w for this lane's columns, fp32 in registers.
     float wf[NV][E];
     {
         const u32x4* wp = static_cast<const u32x4*>(a.w);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int k = 0; k < WCH; ++k) {
-                u32x4 v = (c < nch) ? wp[c * WCH + k] : u32x4{0u, 0u, 0u, 0u};
-                unpack<WT>(v, &wf[i][k * WPER]);
-            }
-        }
+            for (int k = 0; k < WCH; ++k) unpack<WT>(keep_if(cok[i], wp[cix[i] * WCH + k]), &wf[i][k * WPER]);
     }
 
     double acc[NV][E];
@@ -91,41 +84,41 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     const char* xbase = static_cast<const char*>(a.x);
     char* dxbase = static_cast<char*>(a.dx);
 
-    // Software pipeline: the next row's g, x and rstd are loaded while the
-    // current row is reduced and written.
-    u32x4 gn[NV], xn[NV];
-    float rsn;
-    {
-        const int64_t r0 = lo + R.grp;
-        const bool v0 = r0 < hi;
-        bwd_load_row<NV>(gn, reinterpret_cast<const u32x4*>(gbase + r0 * a.lddy * XB), lane, lpr, nch, v0);
-        bwd_load_row<NV>(xn, reinterpret_cast<const u32x4*>(xbase + r0 * a.ldx * XB), lane, lpr, nch, v0);
-        rsn = v0 ? a.rstd[r0] : 0.0f;
-    }
+    struct RowBuf {
+        u32x4 g[NV], x[NV];
+        float rs;
+    };
 
-    for (int it = 0; it < n_it; ++it) {
+    // Rows of this group: lo + grp + it * gpw; past the end of the strip the
+    // address is clamped to the strip's last row, whose values then enter with
+    // rstd = 0 (no dot product, no dw contribution) and are not stored.  The
+    // loaded registers are not touched until they are used, so the next row's
+    // loads stay in flight while the current row is processed.
+    auto load = [&](RowBuf& b, int it) {
+        const int64_t r = lo + R.grp + (int64_t)it * gpw;
+        const int64_t rr = r < hi ? r : hi - 1;
+        b.rs = a.rstd[rr];
+        const u32x4* grow = reinterpret_cast<const u32x4*>(gbase + rr * a.lddy * XB);
+        const u32x4* xrow = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * XB);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            b.g[i] = ld16<NT>(grow + cix[i]);
+            b.x[i] = ld16<NT>(xrow + cix[i]);
+        }
+    };
+
+    auto process = [&](const RowBuf& b, int it) {
         const int64_t r = lo + R.grp + (int64_t)it * gpw;
         const bool valid = r < hi;
-        u32x4 gv[NV], xv[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) { gv[i] = gn[i]; xv[i] = xn[i]; }
-        const float rs = rsn;
-        if (it + 1 < n_it) {
-            const int64_t rn = r + gpw;
-            const bool vn = rn < hi;
-            bwd_load_row<NV>(gn, reinterpret_cast<const u32x4*>(gbase + rn * a.lddy * XB), lane, lpr, nch, vn);
-            bwd_load_row<NV>(xn, reinterpret_cast<const u32x4*>(xbase + rn * a.ldx * XB), lane, lpr, nch, vn);
-            rsn = vn ? a.rstd[rn] : 0.0f;
-        }
-
+        const float rs = valid ? b.rs : 0.0f;
         // dot = sum_j g*w*xhat, and the exact dw contributions of this row.
         const double rsd = (double)rs;
         float dot = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             float g[E], x[E];
-            unpack<XT>(gv[i], g);
-            unpack<XT>(xv[i], x);
+            unpack<XT>(keep_if(cok[i], b.g[i]), g);    // clamped duplicate chunks add nothing
+            unpack<XT>(b.x[i], x);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 dot = __builtin_fmaf(g[e] * wf[i][e], x[e] * rs, dot);
@@ -137,17 +130,33 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         }
         dot = R.sum(dot, red, it);
         const float cm = dot / (float)a.H;
+        if (valid) {
+            u32x4* dxrow = reinterpret_cast<u32x4*>(dxbase + r * a.lddx * XB);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float g[E], x[E], o[E];
+                u32x4 gc = b.g[i], xc = b.x[i];
+                opaque(gc);
+                opaque(xc);
+                unpack<XT>(gc, g);
+                unpack<XT>(xc, x);
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = rs * __builtin_fmaf(-cm, x[e] * rs, g[e] * wf[i][e]);
+                if (cok[i]) st16<NT>(dxrow + cix[i], pack<XT>(o));
+            }
+        }
+    };
 
-        u32x4* dxrow = reinterpret_cast<u32x4*>(dxbase + r * a.lddx * XB);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
-            float g[E], x[E], o[E];
-            unpack<XT>(gv[i], g);
-            unpack<XT>(xv[i], x);
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = rs * __builtin_fmaf(-cm, x[e] * rs, g[e] * wf[i][e]);
-            if (valid && c < nch) dxrow[c] = pack<XT>(o);
+    // Two row buffers in ping-pong: the next row's g, x and rstd are in flight
+    // while the current row is reduced and written.
+    RowBuf b0, b1;
+    load(b0, 0);
+    for (int it = 0; it < n_it; it += 2) {
+        if (it + 1 < n_it) load(b1, it + 1);
+        process(b0, it);
+        if (it + 1 < n_it) {
+            if (it + 2 < n_it) load(b0, it + 2);
+            process(b1, it + 1);
         }
     }
 
@@ -234,7 +243,12 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t n)
 template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET>
 static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    if (p.flags & RN_FLAG_NT)
+        hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true>), dim3((unsigned)p.grid), dim3(p.wgs),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false>), dim3((unsigned)p.grid), dim3(p.wgs),
+                           0, s, a);
     return hipGetLastError();
 }
 

@@ -53,6 +53,18 @@ __device__ __forceinline__ void st8(u32x2* p, u32x2 v)
     else *p = v;
 }
 
+// Make a register value opaque to the optimizer for one use site, so that a
+// loop-invariant packed value is not unpacked once and kept live in its wider
+// form across the loop (which would cost registers, not time).
+__device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Zero a loaded vector when its chunk or row is out of range (the load itself
+// was issued from a clamped, always valid address).
+__device__ __forceinline__ u32x4 keep_if(bool ok, const u32x4& v)
+{
+    return ok ? v : u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  A bf16 value is the upper half of a binary32, so unpacking
 // is a shift or a mask; packing uses v_cvt_pk_bf16_f32 (round to nearest even).

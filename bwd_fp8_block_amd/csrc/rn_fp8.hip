@@ -10,7 +10,8 @@
 //   a re-quantisation of normed_out.
 //
 // Mapping.  One row per group of LPR lanes, rows of a work-group's chunk
-// taken GPW at a time.  Chunk c (8 bf16) belongs to lane c % LPR, so for
+// taken GPW at a time; the next row's x and residual are loaded as soon as
+// the current row's h is formed, overlapping its normalize/quantize/store.  Chunk c (8 bf16) belongs to lane c % LPR, so for
 // LPR in {16, 32, 64, ...} a 1x128 block (16 chunks) is exactly one 16-lane
 // DPP row: the block amax is four DPP max steps on packed-magnitude integers,
 // with no LDS.  The row (h, then n) stays in registers; HBM sees x and
@@ -88,7 +89,7 @@ __device__ __forceinline__ uint32_t chunk_absmax_bits(const u32x4& v)
     return (uint32_t)max(m[0], m[1]);
 }
 
-template <int LPRC, int NV, int WGMAX>
+template <int LPRC, int NV, int WGMAX, bool NT>
 __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
 {
     static_assert(LPRC % 16 == 0, "a 1x128 block must be one 16-lane DPP row");
@@ -103,56 +104,77 @@ __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
     chunk_rows(xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, lo, hi);
     const int n_it = (int)((hi - lo + gpw - 1) / gpw);
 
+    int cix[NV];
+    bool cok[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + lpr * i;
+        cok[i] = c < nch;
+        cix[i] = cok[i] ? c : nch - 1;
+    }
+
     u32x4 wv[NV];
     {
         const u32x4* wp = static_cast<const u32x4*>(a.w);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
-            wv[i] = (c < nch) ? wp[c] : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < NV; ++i) wv[i] = keep_if(cok[i], wp[cix[i]]);
     }
 
     const char* xbase = static_cast<const char*>(a.x);
     char* rbase = static_cast<char*>(a.res);
     char* nbase = static_cast<char*>(a.normed);
 
+    // Loads of a row's x and residual; past the chunk end the address is
+    // clamped to the chunk's last row (nothing is stored for it).  The loaded
+    // registers are left untouched until they are used.
+    u32x4 xv[NV], rv[NV];
+    auto load = [&](int it) {
+        const int64_t r = lo + R.grp + (int64_t)it * gpw;
+        const int64_t rr = r < hi ? r : hi - 1;
+        const u32x4* xrow = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * 2);
+        const u32x4* rrow = reinterpret_cast<const u32x4*>(rbase + rr * a.ldr * 2);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            xv[i] = ld16<NT>(xrow + cix[i]);
+            rv[i] = ld16<NT>(rrow + cix[i]);
+        }
+    };
+
+    load(0);
     for (int it = 0; it < n_it; ++it) {
         const int64_t r = lo + R.grp + (int64_t)it * gpw;
         const bool valid = r < hi;
-        const u32x4* xrow = reinterpret_cast<const u32x4*>(xbase + r * a.ldx * 2);
-        u32x4* rrow = reinterpret_cast<u32x4*>(rbase + r * a.ldr * 2);
 
+        // h = bf16(x + r): the fp32 sum of two bf16 values rounds to the
+        // same bf16 as their exact sum.
         u32x4 hv[NV];
-        {
-            u32x4 xv[NV], rv[NV];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int c = lane + lpr * i;
-                if (valid && c < nch) { xv[i] = xrow[c]; rv[i] = rrow[c]; }
-                else { xv[i] = u32x4{0u, 0u, 0u, 0u}; rv[i] = u32x4{0u, 0u, 0u, 0u}; }
-            }
-            // h = bf16(x + r): the fp32 sum of two bf16 values rounds to the
-            // same bf16 as their exact sum.
+        for (int i = 0; i < NV; ++i) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    hv[i][k] = pack_bf16x2(bf16lo(xv[i][k]) + bf16lo(rv[i][k]),
-                                           bf16hi(xv[i][k]) + bf16hi(rv[i][k]));
+            for (int k = 0; k < 4; ++k)
+                hv[i][k] = pack_bf16x2(bf16lo(xv[i][k]) + bf16lo(rv[i][k]), bf16hi(xv[i][k]) + bf16hi(rv[i][k]));
+            hv[i] = keep_if(cok[i], hv[i]);     // clamped duplicate chunks are zero
         }
+
+        // x and residual of this row are consumed: the next row's loads go
+        // into the same registers and overlap the rest of this row.
+        if (it + 1 < n_it) load(it + 1);
 
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
-            if (valid && c < nch) rrow[c] = hv[i];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float l = bf16lo(hv[i][k]), h = bf16hi(hv[i][k]);
                 ss = __builtin_fmaf(l, l, ss);
                 ss = __builtin_fmaf(h, h, ss);
             }
+        }
+        if (valid) {
+            u32x4* rrow = reinterpret_cast<u32x4*>(rbase + r * a.ldr * 2);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (cok[i]) st16<NT>(rrow + cix[i], hv[i]);
         }
         ss = R.sum(ss, red, it);
         const float rs = 1.0f / __builtin_sqrtf(ss / (float)a.H + a.eps);
@@ -161,20 +183,20 @@ __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
         u32x2* orow = reinterpret_cast<u32x2*>(a.out + r * a.ldo);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
             u32x4 nv;
+            u32x4 wc = wv[i];
+            opaque(wc);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                nv[k] = pack_bf16x2((bf16lo(hv[i][k]) * rs) * bf16lo(wv[i][k]),
-                                    (bf16hi(hv[i][k]) * rs) * bf16hi(wv[i][k]));
+                nv[k] = pack_bf16x2((bf16lo(hv[i][k]) * rs) * bf16lo(wc[k]), (bf16hi(hv[i][k]) * rs) * bf16hi(wc[k]));
             const uint32_t mb = max16_u32(chunk_absmax_bits(nv));
             const float amax = __uint_as_float(mb << 16);
             const float s = amax / 448.0f;
             const u32x2 q = quant_chunk(nv, s);
-            if (valid && c < nch) {
-                nrow[c] = nv;
-                orow[c] = q;
-                if ((lane & 15) == 0) a.scale[(int64_t)(c >> 4) * a.scale_ld + r] = s;
+            if (valid && cok[i]) {
+                st16<NT>(nrow + cix[i], nv);
+                st8<NT>(orow + cix[i], q);
+                if ((lane & 15) == 0) a.scale[(int64_t)(cix[i] >> 4) * a.scale_ld + r] = s;
             }
         }
     }
@@ -186,7 +208,10 @@ __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
 template <int LPRC, int NV, int WGMAX>
 static hipError_t fp8_go(const Fp8Args& a, const Policy& p, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_add_rmsnorm_fp8<LPRC, NV, WGMAX>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    if (p.flags & RN_FLAG_NT)
+        hipLaunchKernelGGL((k_add_rmsnorm_fp8<LPRC, NV, WGMAX, true>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_add_rmsnorm_fp8<LPRC, NV, WGMAX, false>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
     return hipGetLastError();
 }
 

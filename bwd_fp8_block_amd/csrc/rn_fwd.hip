@@ -11,26 +11,17 @@
 // the sum-of-squares pass and the write pass, so x is read from HBM once; w is
 // read once per work-group and kept in registers.  The row reduction is a DPP
 // butterfly inside the wavefront, plus one LDS exchange when a row spans
-// several wavefronts.  With PF the next row's loads are issued before the
-// current row is reduced, so each wavefront keeps two rows of loads in flight.
+// several wavefronts.  Two row buffers alternate, so each wavefront keeps the
+// next row's loads in flight while it reduces and writes the current one.
+// Loads are never predicated: out-of-range chunks and rows load from a
+// clamped in-bounds address and are zeroed, which keeps the loads in one
+// unbranched batch.  NT selects non-temporal (streaming) loads and stores.
 #include "rn_device.h"
 #include "rn_internal.h"
 
 namespace rn {
 
-// Load the NV chunks of one row that this lane owns (zeros when masked off).
-template <int NV, bool NT>
-__device__ __forceinline__ void load_row(u32x4 (&v)[NV], const u32x4* row, int lane, int lpr, int nch, bool valid)
-{
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int c = lane + lpr * i;
-        if (valid && c < nch) v[i] = ld16<NT>(row + c);
-        else v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool PF, bool NTL, bool NTS>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -48,67 +39,87 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     chunk_rows(xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, lo, hi);
     const int n_it = (int)((hi - lo + gpw - 1) / gpw);
 
-    // w for this lane's chunks, raw words kept in registers.
+    // This lane's chunks: index (clamped into the row so that every load is
+    // in bounds) and whether it is real.
+    int cix[NV];
+    bool cok[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + lpr * i;
+        cok[i] = c < nch;
+        cix[i] = cok[i] ? c : nch - 1;
+    }
+
+    // w for this lane's chunks, raw (packed) words kept in registers.
     u32x4 wr[NV][WCH];
     {
         const u32x4* wp = static_cast<const u32x4*>(a.w);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int k = 0; k < WCH; ++k) wr[i][k] = (c < nch) ? wp[c * WCH + k] : u32x4{0u, 0u, 0u, 0u};
-        }
+            for (int k = 0; k < WCH; ++k) wr[i][k] = keep_if(cok[i], wp[cix[i] * WCH + k]);
     }
 
     const char* xbase = static_cast<const char*>(a.x);
     char* ybase = static_cast<char*>(a.y);
 
-    u32x4 nxt[NV];
-    if constexpr (PF) {
-        const int64_t r0 = lo + R.grp;
-        load_row<NV, NTL>(nxt, reinterpret_cast<const u32x4*>(xbase + r0 * a.ldx * XB), lane, lpr, nch, r0 < hi);
-    }
+    // Rows of this group: lo + grp + it * gpw.  Past the end of the chunk the
+    // address is clamped to the chunk's last row (nothing is stored for it).
+    // Loaded registers are not touched until they are used, so the loads of
+    // the next row stay in flight while the current row is processed.
+    auto load = [&](u32x4 (&v)[NV], int it) {
+        const int64_t r = lo + R.grp + (int64_t)it * gpw;
+        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + (r < hi ? r : hi - 1) * a.ldx * XB);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = ld16<NT>(row + cix[i]);
+    };
 
-    for (int it = 0; it < n_it; ++it) {
+    auto process = [&](const u32x4 (&xv)[NV], int it) {
         const int64_t r = lo + R.grp + (int64_t)it * gpw;
         const bool valid = r < hi;
-        u32x4 xv[NV];
-        if constexpr (PF) {
-#pragma unroll
-            for (int i = 0; i < NV; ++i) xv[i] = nxt[i];
-            const int64_t rn = r + gpw;
-            if (it + 1 < n_it)
-                load_row<NV, NTL>(nxt, reinterpret_cast<const u32x4*>(xbase + rn * a.ldx * XB), lane, lpr, nch, rn < hi);
-        } else {
-            load_row<NV, NTL>(xv, reinterpret_cast<const u32x4*>(xbase + r * a.ldx * XB), lane, lpr, nch, valid);
-        }
-
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             float f[E];
-            unpack<XT>(xv[i], f);
+            unpack<XT>(keep_if(cok[i], xv[i]), f);      // clamped duplicate chunks add nothing
 #pragma unroll
             for (int e = 0; e < E; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
         }
         ss = R.sum(ss, red, it);
-
         const float ms = ss / (float)a.H;
         const float rs = 1.0f / __builtin_sqrtf(ms + a.eps);
-
-        u32x4* yrow = reinterpret_cast<u32x4*>(ybase + r * a.ldy * XB);
+        if (valid) {
+            u32x4* yrow = reinterpret_cast<u32x4*>(ybase + r * a.ldy * XB);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
-            float f[E], wf[E], o[E];
-            unpack<XT>(xv[i], f);
+            for (int i = 0; i < NV; ++i) {
+                float f[E], wf[E], o[E];
+                u32x4 xc = xv[i];
+                opaque(xc);               // unpack again rather than keep E floats live
+                unpack<XT>(xc, f);
 #pragma unroll
-            for (int k = 0; k < WCH; ++k) unpack<WT>(wr[i][k], wf + k * WPER);
+                for (int k = 0; k < WCH; ++k) {
+                    opaque(wr[i][k]);
+                    unpack<WT>(wr[i][k], wf + k * WPER);
+                }
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = (f[e] * rs) * wf[e];
-            if (valid && c < nch) st16<NTS>(yrow + c, pack<XT>(o));
+                for (int e = 0; e < E; ++e) o[e] = (f[e] * rs) * wf[e];
+                if (cok[i]) st16<NT>(yrow + cix[i], pack<XT>(o));
+            }
+            if (lane == 0) a.rstd[r] = rs;
         }
-        if (valid && lane == 0) a.rstd[r] = rs;
+    };
+
+    // Two row buffers in ping-pong: the next row's loads are in flight while
+    // the current row is reduced and written.
+    u32x4 b0[NV], b1[NV];
+    load(b0, 0);
+    for (int it = 0; it < n_it; it += 2) {
+        if (it + 1 < n_it) load(b1, it + 1);
+        process(b0, it);
+        if (it + 1 < n_it) {
+            if (it + 2 < n_it) load(b0, it + 2);
+            process(b1, it + 1);
+        }
     }
 }
 
@@ -116,15 +127,13 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 // Variant table and dispatch: template on the group class (16, 32, 64+) and
 // on the vectors per lane; the group width for class 64 is a launch argument.
 // ---------------------------------------------------------------------------
-constexpr bool FWD_PF = true;
-constexpr bool FWD_NTL = false;
-constexpr bool FWD_NTS = false;
-
 template <int XT, int WT, int LPRC, int NV, int WGMAX>
 static hipError_t fwd_go(const FwdArgs& a, const Policy& p, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, FWD_PF, FWD_NTL, FWD_NTS>),
-                       dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    if (p.flags & RN_FLAG_NT)
+        hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
     return hipGetLastError();
 }
 

@@ -60,9 +60,10 @@ int current_device_cu(int* cu)
 
 // ---------------------------------------------------------------------------
 // Optional policy override for tuning sweeps, read once: RN_POLICY_FWD,
-// RN_POLICY_BWD, RN_POLICY_FP8 = "lpr,nv,wgs,grid" (0 keeps the default).
+// RN_POLICY_BWD, RN_POLICY_FP8 = "lpr,nv,wgs,grid[,flags]" (0 keeps the
+// default; flags -1 or absent keeps the default).
 // ---------------------------------------------------------------------------
-struct Override { int lpr = 0, nv = 0, wgs = 0; long long grid = 0; };
+struct Override { int lpr = 0, nv = 0, wgs = 0; long long grid = 0; int flags = -1; };
 Override g_ovr[3];
 std::once_flag g_ovr_once;
 bool g_log = false;
@@ -72,13 +73,19 @@ void read_overrides()
     const char* names[3] = {"RN_POLICY_FWD", "RN_POLICY_BWD", "RN_POLICY_FP8"};
     for (int k = 0; k < 3; ++k) {
         const char* v = std::getenv(names[k]);
-        if (v) std::sscanf(v, "%d,%d,%d,%lld", &g_ovr[k].lpr, &g_ovr[k].nv, &g_ovr[k].wgs, &g_ovr[k].grid);
+        if (v)
+            std::sscanf(v, "%d,%d,%d,%lld,%d", &g_ovr[k].lpr, &g_ovr[k].nv, &g_ovr[k].wgs, &g_ovr[k].grid,
+                        &g_ovr[k].flags);
     }
     const char* l = std::getenv("RN_LOG");
     g_log = l && l[0] == '1';
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Streaming (non-temporal) loads and stores by default: every byte of the
+// row tensors is touched exactly once per call.
+constexpr int RN_FLAG_NT_DEFAULT = rn::RN_FLAG_NT;
 
 // Threads per work-group for a row-group width: as many whole groups as fit
 // in `cap` threads.
@@ -110,6 +117,7 @@ int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
     p->kernel = 0;
+    p->flags = RN_FLAG_NT_DEFAULT;
     return RN_OK;
 }
 
@@ -132,6 +140,7 @@ int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
     p->kernel = 1;
+    p->flags = RN_FLAG_NT_DEFAULT;
     return RN_OK;
 }
 
@@ -151,6 +160,7 @@ int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
     p->kernel = 2;
+    p->flags = RN_FLAG_NT_DEFAULT;
     return RN_OK;
 }
 
@@ -161,8 +171,9 @@ void apply_override(int op, int64_t T, int nch, Policy* p)
 {
     std::call_once(g_ovr_once, read_overrides);
     const Override& o = g_ovr[op];
-    if (!o.lpr && !o.nv && !o.wgs && !o.grid) return;
+    if (!o.lpr && !o.nv && !o.wgs && !o.grid && o.flags < 0) return;
     Policy q = *p;
+    if (o.flags >= 0) q.flags = o.flags;
     if (o.lpr) q.lpr = o.lpr;
     if (o.nv) q.nv = o.nv;
     if (o.wgs) q.wgs = o.wgs;
@@ -283,6 +294,7 @@ int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype, int 
     }
     if (st != RN_OK) return st;
     out[0] = p.lpr; out[1] = p.nv; out[2] = p.wgs; out[3] = (int32_t)p.grid; out[4] = p.gpw; out[5] = p.kernel;
+    out[6] = p.flags;
     return RN_OK;
 }
 

@@ -16,7 +16,10 @@ struct Policy {
     int64_t grid;   // work-groups = row chunks
     int gpw;        // row groups per work-group (rows processed per WG pass)
     int kernel;     // variant id (for logging and tests)
+    int flags;      // RN_FLAG_* bits
 };
+
+constexpr int RN_FLAG_NT = 1;    // non-temporal (streaming) loads and stores
 
 struct FwdArgs {
     int lpr;                     // lanes per row group (runtime for class 64)

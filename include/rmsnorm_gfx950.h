@@ -174,8 +174,9 @@ int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx,
 /*
  * Host-only launch policy query (no HIP call; usable without a GPU).
  * op: 0 = forward, 1 = backward, 2 = fused fp8 producer.
- * Fills out[0..5] = { lanes per row, 16-byte vectors per lane, threads per
- * work-group, work-groups (row chunks), rows per work-group pass, kernel id }
+ * Fills out[0..6] = { lanes per row, 16-byte vectors per lane, threads per
+ * work-group, work-groups (row chunks), rows per work-group pass, kernel id,
+ * flags (bit 0: non-temporal streaming loads/stores) }
  * for a device with `cu_count` compute units.  Returns an rn_status.
  */
 int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype,
