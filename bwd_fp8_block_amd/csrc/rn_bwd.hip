@@ -32,7 +32,7 @@
 
 namespace rn {
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET, bool NT>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET, bool NT, int PD>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -51,9 +51,8 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     const int64_t G = gridDim.x;
     const int64_t strip = xcd_chunk(blockIdx.x, G);
 
-    int64_t lo, hi;
-    chunk_rows(strip, G, a.T, lo, hi);
-    const int n_it = (int)((hi - lo + gpw - 1) / gpw);
+    const RowWalk W = row_walk(a.interleave != 0, strip, G, a.T, gpw, R.grp);
+    const int n_it = W.n_it;
 
     int cix[NV];
     bool cok[NV];
@@ -95,8 +94,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     // loaded registers are not touched until they are used, so the next row's
     // loads stay in flight while the current row is processed.
     auto load = [&](RowBuf& b, int it) {
-        const int64_t r = lo + R.grp + (int64_t)it * gpw;
-        const int64_t rr = r < hi ? r : hi - 1;
+        const int64_t rr = W.clamp(W.row(it));
         b.rs = a.rstd[rr];
         const u32x4* grow = reinterpret_cast<const u32x4*>(gbase + rr * a.lddy * XB);
         const u32x4* xrow = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * XB);
@@ -108,8 +106,8 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     };
 
     auto process = [&](const RowBuf& b, int it) {
-        const int64_t r = lo + R.grp + (int64_t)it * gpw;
-        const bool valid = r < hi;
+        const int64_t r = W.row(it);
+        const bool valid = W.valid(r);
         const float rs = valid ? b.rs : 0.0f;
         // dot = sum_j g*w*xhat, and the exact dw contributions of this row.
         const double rsd = (double)rs;
@@ -147,18 +145,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         }
     };
 
-    // Two row buffers in ping-pong: the next row's g, x and rstd are in flight
-    // while the current row is reduced and written.
-    RowBuf b0, b1;
-    load(b0, 0);
-    for (int it = 0; it < n_it; it += 2) {
-        if (it + 1 < n_it) load(b1, it + 1);
-        process(b0, it);
-        if (it + 1 < n_it) {
-            if (it + 2 < n_it) load(b0, it + 2);
-            process(b1, it + 1);
-        }
-    }
+    // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in
+    // flight while the current row is reduced and written.
+    row_pipeline<PD, RowBuf>(n_it, load, process);
 
     // Emit this strip's dw partial: the gpw row groups' accumulators are
     // combined in a fixed order (group 0, 1, ...) in FP64 and rounded once to
@@ -243,12 +232,24 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t n)
 template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET>
 static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
 {
-    if (p.flags & RN_FLAG_NT)
-        hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true>), dim3((unsigned)p.grid), dim3(p.wgs),
-                           0, s, a);
-    else
-        hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false>), dim3((unsigned)p.grid), dim3(p.wgs),
-                           0, s, a);
+    const dim3 g((unsigned)p.grid), b(p.wgs);
+    const int pd = (p.flags >> 4) & 7;
+    const bool nt = (p.flags & RN_FLAG_NT) != 0;
+    if constexpr (LPRC == 64 && NV == 1) {
+        // the main variant: pipeline depth is a launch choice
+        if (pd == 3) {
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true, 3>), g, b, 0, s, a);
+            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false, 3>), g, b, 0, s, a);
+            return hipGetLastError();
+        }
+        if (pd == 4) {
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true, 4>), g, b, 0, s, a);
+            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false, 4>), g, b, 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true, 2>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false, 2>), g, b, 0, s, a);
     return hipGetLastError();
 }
 

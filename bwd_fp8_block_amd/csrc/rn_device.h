@@ -208,6 +208,30 @@ __device__ __forceinline__ uint32_t max16_u32(uint32_t v)
     return v;
 }
 
+// Software pipeline over the rows of a row group: PD row buffers in a ring,
+// PD-1 rows of loads in flight while one row is processed.  All buffer
+// indices are compile-time constants after unrolling; the branches depend
+// only on n_it, which is uniform across the work-group, so `process` may
+// contain barriers.  load(buf, it) issues the loads of iteration `it`;
+// process(buf, it) consumes them.
+template <int PD, class Buf, class LoadF, class ProcF>
+__device__ __forceinline__ void row_pipeline(int n_it, LoadF&& load, ProcF&& process)
+{
+    Buf b[PD];
+#pragma unroll
+    for (int k = 0; k < PD - 1; ++k)
+        if (k < n_it) load(b[k], k);
+    for (int it = 0; it < n_it; it += PD) {
+#pragma unroll
+        for (int k = 0; k < PD; ++k) {
+            if (it + k < n_it) {
+                if (it + k + PD - 1 < n_it) load(b[(k + PD - 1) % PD], it + k + PD - 1);
+                process(b[k], it + k);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Work partition helpers.
 // ---------------------------------------------------------------------------
@@ -230,6 +254,42 @@ __device__ __forceinline__ void chunk_rows(int64_t g, int64_t G, int64_t T, int6
 {
     lo = (g * T) / G;
     hi = ((g + 1) * T) / G;
+}
+
+// The rows a row group visits: row(it) = first + it * step for it < n_it;
+// rows at or past `limit` are padding (their loads use the clamped row
+// limit - 1, which is always a real row, and nothing is stored for them).
+//   contiguous:  work-group L owns the chunk [lo, hi) of rows; its gpw groups
+//                interleave inside it (first = lo + grp, step = gpw).
+//   interleaved: at iteration it the work-groups cover the rows
+//                [it*G*gpw, (it+1)*G*gpw) together, so the GPU streams through
+//                the tensor as one moving window; L is XCD-aware, so each
+//                XCD's share of the window is contiguous.
+struct RowWalk {
+    int64_t first, step, limit;
+    int n_it;
+    __device__ __forceinline__ int64_t row(int it) const { return first + (int64_t)it * step; }
+    __device__ __forceinline__ bool valid(int64_t r) const { return r < limit; }
+    __device__ __forceinline__ int64_t clamp(int64_t r) const { return r < limit ? r : limit - 1; }
+};
+
+__device__ __forceinline__ RowWalk row_walk(bool interleaved, int64_t L, int64_t G, int64_t T, int gpw, int grp)
+{
+    RowWalk w;
+    if (interleaved) {
+        w.first = L * gpw + grp;
+        w.step = G * gpw;
+        w.limit = T;
+        w.n_it = (int)((T - L * gpw + w.step - 1) / w.step);
+    } else {
+        int64_t lo, hi;
+        chunk_rows(L, G, T, lo, hi);
+        w.first = lo + grp;
+        w.step = gpw;
+        w.limit = hi;
+        w.n_it = (int)((hi - lo + gpw - 1) / gpw);
+    }
+    return w;
 }
 
 } // namespace rn

@@ -100,9 +100,8 @@ __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
     const int lane = R.lane, lpr = R.lpr, gpw = R.gpw;
     const int nch = a.nch;
 
-    int64_t lo, hi;
-    chunk_rows(xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, lo, hi);
-    const int n_it = (int)((hi - lo + gpw - 1) / gpw);
+    const RowWalk W = row_walk(a.interleave != 0, xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, gpw, R.grp);
+    const int n_it = W.n_it;
 
     int cix[NV];
     bool cok[NV];
@@ -129,8 +128,7 @@ __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
     // registers are left untouched until they are used.
     u32x4 xv[NV], rv[NV];
     auto load = [&](int it) {
-        const int64_t r = lo + R.grp + (int64_t)it * gpw;
-        const int64_t rr = r < hi ? r : hi - 1;
+        const int64_t rr = W.clamp(W.row(it));
         const u32x4* xrow = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * 2);
         const u32x4* rrow = reinterpret_cast<const u32x4*>(rbase + rr * a.ldr * 2);
 #pragma unroll
@@ -142,8 +140,8 @@ __global__ __launch_bounds__(WGMAX) void k_add_rmsnorm_fp8(Fp8Args a)
 
     load(0);
     for (int it = 0; it < n_it; ++it) {
-        const int64_t r = lo + R.grp + (int64_t)it * gpw;
-        const bool valid = r < hi;
+        const int64_t r = W.row(it);
+        const bool valid = W.valid(r);
 
         // h = bf16(x + r): the fp32 sum of two bf16 values rounds to the
         // same bf16 as their exact sum.

@@ -21,7 +21,7 @@
 
 namespace rn {
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -35,9 +35,8 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     const int lane = R.lane, lpr = R.lpr, gpw = R.gpw;
     const int nch = a.nch;
 
-    int64_t lo, hi;
-    chunk_rows(xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, lo, hi);
-    const int n_it = (int)((hi - lo + gpw - 1) / gpw);
+    const RowWalk W = row_walk(a.interleave != 0, xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, gpw, R.grp);
+    const int n_it = W.n_it;
 
     // This lane's chunks: index (clamped into the row so that every load is
     // in bounds) and whether it is real.
@@ -67,16 +66,19 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     // address is clamped to the chunk's last row (nothing is stored for it).
     // Loaded registers are not touched until they are used, so the loads of
     // the next row stay in flight while the current row is processed.
-    auto load = [&](u32x4 (&v)[NV], int it) {
-        const int64_t r = lo + R.grp + (int64_t)it * gpw;
-        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + (r < hi ? r : hi - 1) * a.ldx * XB);
+    struct RowBuf {
+        u32x4 v[NV];
+    };
+    auto load = [&](RowBuf& b, int it) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + W.clamp(W.row(it)) * a.ldx * XB);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = ld16<NT>(row + cix[i]);
+        for (int i = 0; i < NV; ++i) b.v[i] = ld16<NT>(row + cix[i]);
     };
 
-    auto process = [&](const u32x4 (&xv)[NV], int it) {
-        const int64_t r = lo + R.grp + (int64_t)it * gpw;
-        const bool valid = r < hi;
+    auto process = [&](const RowBuf& b, int it) {
+        const u32x4 (&xv)[NV] = b.v;
+        const int64_t r = W.row(it);
+        const bool valid = W.valid(r);
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -109,18 +111,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
         }
     };
 
-    // Two row buffers in ping-pong: the next row's loads are in flight while
+    // PD row buffers in a ring: the next PD-1 rows' loads are in flight while
     // the current row is reduced and written.
-    u32x4 b0[NV], b1[NV];
-    load(b0, 0);
-    for (int it = 0; it < n_it; it += 2) {
-        if (it + 1 < n_it) load(b1, it + 1);
-        process(b0, it);
-        if (it + 1 < n_it) {
-            if (it + 2 < n_it) load(b0, it + 2);
-            process(b1, it + 1);
-        }
-    }
+    row_pipeline<PD, RowBuf>(n_it, load, process);
 }
 
 // ---------------------------------------------------------------------------
@@ -130,10 +123,18 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 template <int XT, int WT, int LPRC, int NV, int WGMAX>
 static hipError_t fwd_go(const FwdArgs& a, const Policy& p, hipStream_t s)
 {
-    if (p.flags & RN_FLAG_NT)
-        hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false>), dim3((unsigned)p.grid), dim3(p.wgs), 0, s, a);
+    const dim3 g((unsigned)p.grid), b(p.wgs);
+    const bool nt = (p.flags & RN_FLAG_NT) != 0;
+    if constexpr (NV <= 4) {
+        // short per-lane rows: a third row buffer is affordable
+        if (((p.flags >> 4) & 7) == 3) {
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 3>), g, b, 0, s, a);
+            else hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 3>), g, b, 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 2>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 2>), g, b, 0, s, a);
     return hipGetLastError();
 }
 

@@ -188,7 +188,7 @@ void apply_override(int op, int64_t T, int nch, Policy* p)
                   : op == 1 ? rn::bwd_variant_exists(lprc, q.nv, q.wgs)
                             : rn::fp8_variant_exists(lprc, q.nv, q.wgs);
     if (!ok) return;
-    if (o.grid) q.grid = o.grid;
+    if (o.grid) q.grid = std::max<int64_t>(1, std::min<int64_t>(o.grid, ceil_div(T, q.gpw)));
     else q.grid = std::max<int64_t>(1, std::min<int64_t>(p->grid * p->gpw / q.gpw, ceil_div(T, q.gpw)));
     if (op == 1 && q.grid > p->grid) q.grid = p->grid;   // workspace is sized for the default
     *p = q;
@@ -350,7 +350,7 @@ int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype, const void* w, int w_dt
     log_policy("fwd", T, H, p);
 
     rn::FwdArgs a{};
-    a.lpr = p.lpr; a.x = x; a.ldx = ldx; a.w = w; a.y = y; a.ldy = ldy; a.rstd = rstd;
+    a.lpr = p.lpr; a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0; a.x = x; a.ldx = ldx; a.w = w; a.y = y; a.ldy = ldy; a.rstd = rstd;
     a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype)); a.eps = eps;
     clear_last_error();
     if (rn::launch_fwd(a, x_dtype, w_dtype, p, (hipStream_t)stream) != hipSuccess) return RN_ERR_LAUNCH;
@@ -412,7 +412,7 @@ int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_
     log_policy(deterministic ? "bwd(det)" : "bwd", T, H, p);
 
     rn::BwdArgs a{};
-    a.lpr = p.lpr; a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.w = w; a.rstd = rstd;
+    a.lpr = p.lpr; a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0; a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.w = w; a.rstd = rstd;
     a.dx = dx; a.lddx = lddx; a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype));
     if (deterministic) {
         a.part = static_cast<float*>(workspace);
@@ -462,7 +462,7 @@ int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx, void* residual, int6
     log_policy("fp8", T, H, p);
 
     rn::Fp8Args a{};
-    a.lpr = p.lpr; a.x = x; a.ldx = ldx; a.res = residual; a.ldr = ldr; a.w = w; a.out = out; a.ldo = ldo;
+    a.lpr = p.lpr; a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0; a.x = x; a.ldx = ldx; a.res = residual; a.ldr = ldr; a.w = w; a.out = out; a.ldo = ldo;
     a.scale = block_scale; a.scale_ld = scale_ld; a.normed = normed_out; a.ldn = ldn;
     a.T = T; a.H = (int)H; a.nch = (int)(H / 8); a.eps = eps;
     clear_last_error();

@@ -20,9 +20,11 @@ struct Policy {
 };
 
 constexpr int RN_FLAG_NT = 1;    // non-temporal (streaming) loads and stores
+constexpr int RN_FLAG_ILV = 2;   // interleaved row order (see RowWalk)
 
 struct FwdArgs {
-    int lpr;                     // lanes per row group (runtime for class 64)
+    int lpr;
+    int interleave;              // RN_FLAG_ILV set in the policy                     // lanes per row group (runtime for class 64)
     const void* x; int64_t ldx;
     const void* w;
     void* y; int64_t ldy;
@@ -33,6 +35,7 @@ struct FwdArgs {
 
 struct BwdArgs {
     int lpr;
+    int interleave;              // RN_FLAG_ILV set in the policy
     const void* dy; int64_t lddy;
     const void* x; int64_t ldx;
     const void* w;
@@ -50,6 +53,7 @@ struct ReduceArgs {
 
 struct Fp8Args {
     int lpr;
+    int interleave;              // RN_FLAG_ILV set in the policy
     const void* x; int64_t ldx;
     void* res; int64_t ldr;
     const void* w;
