@@ -22,6 +22,7 @@ __all__ = [
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes", "add_rmsnorm_fp8_block_quant",
     "rn_query_policy", "rn_bwd_workspace_bytes_for", "rn_status_string", "rn_version",
     "rn_selftest_quant", "rn_selftest_cvt_e4m3",
+    "plan_rmsnorm_fwd", "plan_rmsnorm_bwd", "plan_add_rmsnorm_fp8_block_quant",
 ]
 
 RN_F32 = 0
@@ -145,8 +146,7 @@ def _on(dev: torch.device):
     return _NOSWITCH if dev.index == torch.cuda.current_device() else torch.cuda.device(dev)
 
 
-def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.Tensor, eps: float) -> None:
-    """y = x * rstd * w with rstd = 1/sqrt(mean(x^2) + eps); writes y [T,H] and rstd [T] (fp32)."""
+def _prep_fwd(x, w, y, rstd, eps):
     dev = _dev((x, w, y, rstd))
     T, H = x.shape
     if y.shape != x.shape or y.dtype != x.dtype or w.shape != (H,) or rstd.shape != (T,) or rstd.dtype != torch.float32:
@@ -154,13 +154,20 @@ def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.T
     px, ldx = _mat(x, "x")
     py, ldy = _mat(y, "y")
     with _on(dev):
-        st = lib.rmsnorm_fwd(px, ldx, _dt(x), _vec(w, "w"), _dt(w), py, ldy, _vec(rstd, "rstd"),
-                             T, H, float(eps), _stream(dev))
+        args = (px, ldx, _dt(x), _vec(w, "w"), _dt(w), py, ldy, _vec(rstd, "rstd"), T, H, float(eps), _stream(dev))
+    return dev, lib.rmsnorm_fwd, args
+
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.Tensor, eps: float) -> None:
+    """y = x * rstd * w with rstd = 1/sqrt(mean(x^2) + eps); writes y [T,H] and rstd [T] (fp32)."""
+    dev, fn, args = _prep_fwd(x, w, y, rstd, eps)
+    with _on(dev):
+        st = fn(*args)
     _check("rmsnorm_fwd", st)
 
 
 def rmsnorm_bwd_workspace_bytes(T: int, H: int, device=None) -> int:
-    """Workspace bytes a deterministic rmsnorm_bwd needs for (T, H) on `device`."""
+    """Workspace bytes rmsnorm_bwd needs for (T, H) on `device`."""
     if device is None:
         device = torch.cuda.current_device()
     idx = torch.device(device).index if not isinstance(device, int) else device
@@ -175,7 +182,16 @@ def rmsnorm_bwd_workspace_bytes(T: int, H: int, device=None) -> int:
 def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor,
                 dx: torch.Tensor, dw: torch.Tensor, deterministic: bool = True,
                 workspace: torch.Tensor | None = None) -> None:
-    """dx [T,H] and dw [H] (fp32, overwritten) from dy, x, w and the forward's rstd."""
+    """dx [T,H] and dw [H] (fp32, overwritten) from dy, x, w and the forward's rstd.
+    `workspace`: a device tensor of at least rmsnorm_bwd_workspace_bytes(T, H) bytes
+    (required whenever T > 0; its content does not matter)."""
+    dev, fn, args = _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, workspace)
+    with _on(dev):
+        st = fn(*args)
+    _check("rmsnorm_bwd", st)
+
+
+def _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, workspace):
     dev = _dev((dy, x, w, rstd, dx, dw, workspace))
     T, H = x.shape
     if dy.shape != x.shape or dx.shape != x.shape or dy.dtype != x.dtype or dx.dtype != x.dtype:
@@ -191,9 +207,9 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
             raise ValueError("workspace must be contiguous")
         wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with _on(dev):
-        st = lib.rmsnorm_bwd(pdy, lddy, px, ldx, _dt(x), _vec(w, "w"), _dt(w), _vec(rstd, "rstd"),
-                             pdx, lddx, _vec(dw, "dw"), T, H, 1 if deterministic else 0, wsp, wsb, _stream(dev))
-    _check("rmsnorm_bwd", st)
+        args = (pdy, lddy, px, ldx, _dt(x), _vec(w, "w"), _dt(w), _vec(rstd, "rstd"),
+                pdx, lddx, _vec(dw, "dw"), T, H, 1 if deterministic else 0, wsp, wsb, _stream(dev))
+    return dev, lib.rmsnorm_bwd, args
 
 
 def add_rmsnorm_fp8_block_quant(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor,
@@ -202,6 +218,13 @@ def add_rmsnorm_fp8_block_quant(x: torch.Tensor, residual: torch.Tensor, w: torc
     """residual <- bf16(x + residual); normed_out = bf16 RMSNorm(residual) * w;
     out = e4m3 codes [T,H] (uint8 or float8_e4m3fn); block_scale [H/128, ld] fp32 with
     entry (k, m) the scale of row m, block k (ld = block_scale.stride(0) >= T)."""
+    dev, fn, args = _prep_fp8(x, residual, w, out, block_scale, normed_out, eps)
+    with _on(dev):
+        st = fn(*args)
+    _check("add_rmsnorm_fp8_block_quant", st)
+
+
+def _prep_fp8(x, residual, w, out, block_scale, normed_out, eps):
     dev = _dev((x, residual, w, out, block_scale, normed_out))
     T, H = x.shape
     for t, n in ((x, "x"), (residual, "residual"), (w, "w"), (normed_out, "normed_out")):
@@ -221,10 +244,38 @@ def add_rmsnorm_fp8_block_quant(x: torch.Tensor, residual: torch.Tensor, w: torc
     po, ldo = _mat(out, "out")
     pn, ldn = _mat(normed_out, "normed_out")
     with _on(dev):
-        st = lib.add_rmsnorm_fp8_block_quant(px, ldx, pr, ldr, _vec(w, "w"), po, ldo,
-                                             block_scale.data_ptr(), scale_ld, pn, ldn,
-                                             T, H, float(eps), _stream(dev))
-    _check("add_rmsnorm_fp8_block_quant", st)
+        args = (px, ldx, pr, ldr, _vec(w, "w"), po, ldo, block_scale.data_ptr(), scale_ld, pn, ldn,
+                T, H, float(eps), _stream(dev))
+    return dev, lib.add_rmsnorm_fp8_block_quant, args
+
+
+def _plan(name, prep):
+    dev, fn, args = prep
+    cur = torch.cuda.current_device
+
+    def call() -> None:
+        if dev.index != cur():
+            raise RuntimeError("%s: planned for %s, current device differs" % (name, dev))
+        st = fn(*args)
+        if st:
+            raise RNError(name, st)
+    return call
+
+
+def plan_rmsnorm_fwd(x, w, y, rstd, eps):
+    """A zero-argument callable that runs rmsnorm_fwd on these tensors and torch's current
+    stream at plan time (arguments marshalled once; for launch-bound loops)."""
+    return _plan("rmsnorm_fwd", _prep_fwd(x, w, y, rstd, eps))
+
+
+def plan_rmsnorm_bwd(dy, x, w, rstd, dx, dw, deterministic=True, workspace=None):
+    """Planned rmsnorm_bwd (see plan_rmsnorm_fwd)."""
+    return _plan("rmsnorm_bwd", _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, workspace))
+
+
+def plan_add_rmsnorm_fp8_block_quant(x, residual, w, out, block_scale, normed_out, eps):
+    """Planned add_rmsnorm_fp8_block_quant (see plan_rmsnorm_fwd)."""
+    return _plan("add_rmsnorm_fp8_block_quant", _prep_fp8(x, residual, w, out, block_scale, normed_out, eps))
 
 
 def rn_query_policy(op: int, T: int, H: int, x_dtype: int, w_dtype: int, cu_count: int) -> dict:

@@ -22,17 +22,18 @@
 // gfx950 FP64 FMA issues at the same rate as fp32 FMA, so plain FP64
 // accumulation is the cheaper way to the same end.
 //
-// Deterministic mode: each strip writes its fp32 partial row to the
-// workspace, and a second kernel sums the G partials of every column in a
-// fixed order in FP64 (no atomics: the result depends only on T, H and G).
-// Non-deterministic mode: dw is zeroed by a fill kernel and each strip adds
-// its partial with hardware fp32 atomics.
+// Each strip writes its fp32 partial row to the workspace, and a second
+// kernel sums the G partials of every column in a fixed order in FP64 (no
+// atomics: the result depends only on T, H and G, and is bitwise repeatable).
+// Adding the strip partials with fp32 atomics instead was measured over the
+// per-element dw budget at T = 65536, H = 5120 (1.03x), and was not faster
+// than this second kernel, so both modes of the entry point use this path.
 #include "rn_device.h"
 #include "rn_internal.h"
 
 namespace rn {
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET, bool NT, int PD>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -63,15 +64,23 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         cix[i] = cok[i] ? c : nch - 1;
     }
 
-    // w for this lane's columns, fp32 in registers.
-    float wf[NV][E];
+    // w for this lane's columns: packed words in registers, unpacked at use.
+    u32x4 wr[NV][WCH];
     {
         const u32x4* wp = static_cast<const u32x4*>(a.w);
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int k = 0; k < WCH; ++k) unpack<WT>(keep_if(cok[i], wp[cix[i] * WCH + k]), &wf[i][k * WPER]);
+            for (int k = 0; k < WCH; ++k) wr[i][k] = keep_if(cok[i], wp[cix[i] * WCH + k]);
     }
+    auto w_of = [&](int i, float* wf) {
+#pragma unroll
+        for (int k = 0; k < WCH; ++k) {
+            u32x4 t = wr[i][k];
+            opaque(t);
+            unpack<WT>(t, wf + k * WPER);
+        }
+    };
 
     double acc[NV][E];
 #pragma unroll
@@ -109,37 +118,43 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         const int64_t r = W.row(it);
         const bool valid = W.valid(r);
         const float rs = valid ? b.rs : 0.0f;
-        // dot = sum_j g*w*xhat, and the exact dw contributions of this row.
+        // s = sum_j g*w*x (the row's dot product is rstd * s), and the exact
+        // dw contributions of this row.
         const double rsd = (double)rs;
-        float dot = 0.0f;
+        float sgwx = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            float g[E], x[E];
+            float g[E], x[E], wf[E];
             unpack<XT>(keep_if(cok[i], b.g[i]), g);    // clamped duplicate chunks add nothing
             unpack<XT>(b.x[i], x);
+            w_of(i, wf);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                dot = __builtin_fmaf(g[e] * wf[i][e], x[e] * rs, dot);
+                sgwx = __builtin_fmaf(g[e] * wf[e], x[e], sgwx);
                 if constexpr (XT == DT_BF16)
                     acc[i][e] = __builtin_fma((double)(g[e] * x[e]), rsd, acc[i][e]);
                 else
                     acc[i][e] = __builtin_fma((double)g[e] * (double)x[e], rsd, acc[i][e]);
             }
         }
-        dot = R.sum(dot, red, it);
-        const float cm = dot / (float)a.H;
+        sgwx = R.sum(sgwx, red, it);
+        // dx = rstd*(g*w - c*xhat) with c = rstd*s/H and xhat = rstd*x:
+        //    = rstd*(g*w) - (c*rstd*rstd)*x
+        const float cm = rs * sgwx * a.inv_h;
+        const float k2 = cm * rs * rs;
         if (valid) {
             u32x4* dxrow = reinterpret_cast<u32x4*>(dxbase + r * a.lddx * XB);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                float g[E], x[E], o[E];
+                float g[E], x[E], wf[E], o[E];
                 u32x4 gc = b.g[i], xc = b.x[i];
                 opaque(gc);
                 opaque(xc);
                 unpack<XT>(gc, g);
                 unpack<XT>(xc, x);
+                w_of(i, wf);
 #pragma unroll
-                for (int e = 0; e < E; ++e) o[e] = rs * __builtin_fmaf(-cm, x[e] * rs, g[e] * wf[i][e]);
+                for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(rs, g[e] * wf[e], -k2 * x[e]);
                 if (cok[i]) st16<NT>(dxrow + cix[i], pack<XT>(o));
             }
         }
@@ -162,8 +177,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                 for (int e = 0; e < E; ++e) {
                     const float p = (float)acc[i][e];
                     const int64_t col = (int64_t)c * E + e;
-                    if constexpr (DET) part[strip * a.H + col] = p;
-                    else unsafeAtomicAdd(&part[col], p);
+                    part[strip * a.H + col] = p;
                 }
             }
         }
@@ -184,8 +198,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                     for (int q = 0; q < gpw; ++q) s += stage[(q * lpr + l) * HALF + e];
                     const float p = (float)s;
                     const int64_t col = (int64_t)c * E + h0 + e;
-                    if constexpr (DET) part[strip * a.H + col] = p;
-                    else unsafeAtomicAdd(&part[col], p);
+                    part[strip * a.H + col] = p;
                 }
             }
             __syncthreads();
@@ -229,7 +242,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t n)
 // ---------------------------------------------------------------------------
 // Variant table and dispatch.
 // ---------------------------------------------------------------------------
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool DET>
+template <int XT, int WT, int LPRC, int NV, int WGMAX>
 static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
 {
     const dim3 g((unsigned)p.grid), b(p.wgs);
@@ -238,23 +251,23 @@ static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
     if constexpr (LPRC == 64 && NV == 1) {
         // the main variant: pipeline depth is a launch choice
         if (pd == 3) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true, 3>), g, b, 0, s, a);
-            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false, 3>), g, b, 0, s, a);
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3>), g, b, 0, s, a);
+            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3>), g, b, 0, s, a);
             return hipGetLastError();
         }
         if (pd == 4) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true, 4>), g, b, 0, s, a);
-            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false, 4>), g, b, 0, s, a);
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4>), g, b, 0, s, a);
+            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4>), g, b, 0, s, a);
             return hipGetLastError();
         }
     }
-    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, true, 2>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, DET, false, 2>), g, b, 0, s, a);
+    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 2>), g, b, 0, s, a);
     return hipGetLastError();
 }
 
 // (group class, vectors per lane, largest work-group) triples compiled.
-#define RN_BWD_VARIANTS(X) X(16, 1, 1024) X(32, 1, 1024) X(64, 1, 1024) X(64, 2, 1024)
+#define RN_BWD_VARIANTS(X) X(16, 1, 1024) X(32, 1, 1024) X(64, 1, 1024) X(64, 2, 512) X(64, 2, 1024)
 
 bool bwd_variant_exists(int lprc, int nv, int wgs)
 {
@@ -264,27 +277,21 @@ bool bwd_variant_exists(int lprc, int nv, int wgs)
     return false;
 }
 
-template <int XT, int WT, bool DET>
+template <int XT, int WT>
 static hipError_t bwd_dispatch(const BwdArgs& a, const Policy& p, hipStream_t s)
 {
     const int lprc = p.lpr < 64 ? p.lpr : 64;
-#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return bwd_go<XT, WT, C, N, W, DET>(a, p, s);
+#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return bwd_go<XT, WT, C, N, W>(a, p, s);
     RN_BWD_VARIANTS(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, bool det, const Policy& p, hipStream_t s)
+hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s)
 {
-    if (det) {
-        if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16, true>(a, p, s);
-        if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32, true>(a, p, s);
-        if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32, true>(a, p, s);
-    } else {
-        if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16, false>(a, p, s);
-        if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32, false>(a, p, s);
-        if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32, false>(a, p, s);
-    }
+    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32>(a, p, s);
+    if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32>(a, p, s);
     return hipErrorInvalidValue;
 }
 

@@ -141,7 +141,7 @@ static hipError_t fwd_go(const FwdArgs& a, const Policy& p, hipStream_t s)
 // (group class, vectors per lane, largest work-group) triples compiled.
 #define RN_FWD_VARIANTS(X) X(16, 1, 256) X(16, 2, 256) X(16, 4, 256) X(32, 2, 256) X(32, 4, 256)         \
     X(64, 1, 256) X(64, 2, 256) X(64, 3, 256) X(64, 4, 256) X(64, 5, 256) X(64, 6, 256) X(64, 7, 256) \
-    X(64, 8, 256) X(64, 8, 512)
+    X(64, 8, 256) X(64, 5, 512) X(64, 6, 512) X(64, 7, 512) X(64, 8, 512)
 
 bool fwd_variant_exists(int lprc, int nv, int wgs)
 {

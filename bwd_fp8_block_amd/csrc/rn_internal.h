@@ -41,8 +41,9 @@ struct BwdArgs {
     const void* w;
     const float* rstd;
     void* dx; int64_t lddx;
-    float* part;                 // det: workspace [grid][H]; non-det: dw [H]
+    float* part;                 // workspace [grid][H]: one fp32 dw partial per row strip
     int64_t T; int H; int nch;
+    float inv_h;                 // 1/H rounded to fp32
 };
 
 struct ReduceArgs {
@@ -66,7 +67,7 @@ struct Fp8Args {
 
 // Launchers return hipSuccess or the launch error.  They assume validated args.
 hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, bool det, const Policy& p, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_fp8(const Fp8Args& a, const Policy& p, hipStream_t s);

@@ -100,9 +100,8 @@ int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype,
                 int64_t T, int64_t H, float eps, void* stream);
 
 /*
- * Size in bytes of the workspace that a deterministic rmsnorm_bwd needs for
- * (T, H) on HIP device `device` (fp32 partial sums, one row of H per row
- * chunk).  The value never decreases with T, so a workspace sized for the
+ * Size in bytes of the workspace that rmsnorm_bwd needs for (T, H) on HIP
+ * device `device` (fp32 partial sums, one row of H per row strip).  The value never decreases with T, so a workspace sized for the
  * largest T can be reused for every smaller T.  Returns 0 for T == 0 and
  * (size_t)-1 on invalid arguments or when the device cannot be queried.
  */
@@ -116,16 +115,18 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t H, int device);
  *   dx[r,j] = round_dtype( rstd[r] * (dy[r,j] * w[j] - c[r] * xhat[r,j]) )
  *   dw[j]   = sum_r dy[r,j] * x[r,j] * rstd[r]                (fp32 result)
  * rstd is the forward's stored fp32 value.  dw is OVERWRITTEN.  Each row
- * chunk's dw partial is accumulated per column in FP64 from exact products
- * and rounded once to fp32; the chunk partials are then summed per column in
- * FP64 and rounded once more.
- *   deterministic != 0: the partials go to `workspace` and a second kernel
- *     sums them in a fixed order, so dw is bitwise identical from call to call
- *     (the order depends only on T, H and the device's CU count).  Needs
- *     workspace_bytes >= rmsnorm_bwd_workspace_bytes(T, H, device), else
- *     RN_ERR_WORKSPACE; the workspace content on entry does not matter.
- *   deterministic == 0: dw is zeroed on the stream and the partials are added
- *     with fp32 atomics (order not fixed); workspace may be NULL.
+ * strip's dw partial is accumulated per column in FP64 from exact products
+ * and rounded once to fp32 into `workspace`; a second kernel then sums the
+ * strip partials of every column in a fixed order in FP64 and rounds once
+ * more.  dw is therefore bitwise identical from call to call (the order
+ * depends only on T, H and the device's CU count), and every element is
+ * within 1e-4 + 1e-4*|ref| of the FP64 sum ([M] Summary).
+ *   deterministic: accepted for interface compatibility; both values run the
+ *     fixed-order reduction above (adding strip partials with fp32 atomics
+ *     was measured over the dw budget at T = 65536, and was not faster).
+ *   workspace: device memory of at least rmsnorm_bwd_workspace_bytes(T, H,
+ *     device) bytes, 16-byte aligned, else RN_ERR_WORKSPACE; its content on
+ *     entry does not matter and is garbage on return.
  *   dy [T, lddy] x_dtype; x [T, ldx] x_dtype; w [H] w_dtype; rstd [T] fp32
  *   dx [T, lddx] x_dtype output; dw [H] fp32 output.
  */

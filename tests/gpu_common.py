@@ -1,7 +1,7 @@
 """Helpers shared by the GPU parity tests: host <-> device transfer of the
 workload arrays, and the comparison rules.
 
-Tolerances (north star of this library; readings in the design notes):
+Tolerances (the readings recorded in the design notes):
   fp32 y / dx           |gpu - oracle_fp64| <= 1e-5 (absolute)
   bf16 y / dx / normed  |gpu - oracle_fp64| <= 5e-2 (absolute), and, as a
                         quality check, within one bf16 spacing of the value

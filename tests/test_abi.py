@@ -61,6 +61,7 @@ CU = 256
     (1, 58497, 2048, 1, 0), (0, 65536, 5120, 1, 0), (1, 65536, 5120, 1, 0),
     (2, 4096, 7168, 1, 1), (2, 8192, 4096, 1, 1), (2, 3, 1152, 1, 1), (2, 1, 128, 1, 1),
     (0, 5, 8, 1, 1), (1, 5, 8, 1, 1), (0, 100, 32768, 1, 1), (1, 9, 16384, 1, 1), (2, 9, 32768, 1, 1),
+    (0, 7, 17408, 1, 1), (2, 7, 17408, 1, 1), (0, 7, 9216, 0, 0), (2, 7, 9216, 1, 1), (0, 3, 20480, 1, 0),
 ])
 def test_policy_invariants(rn, op, T, H, xd, wd):
     p = rn.rn_query_policy(op, T, H, xd, wd, CU)
@@ -73,16 +74,24 @@ def test_policy_invariants(rn, op, T, H, xd, wd):
     assert 1 <= p["grid"] <= max(1, -(-T // p["gpw"]))       # no work-group without rows
     if op == 2:
         assert p["lpr"] % 16 == 0                            # 1x128 block = 16 lanes
+    # a compiled variant serves it: the same check the library applies to overrides
+    lprc = min(p["lpr"], 64)
+    if op in (0, 2):
+        assert (lprc, p["nv"]) in {(16, 1), (16, 2), (16, 4), (32, 1), (32, 2), (32, 4)} or \
+            (lprc == 64 and (p["wgs"] <= 256 and 1 <= p["nv"] <= 8 or p["wgs"] <= 512 and 5 <= p["nv"] <= 8))
+    else:
+        assert (lprc, p["nv"]) in {(16, 1), (32, 1), (64, 1), (64, 2)}
     if op == 1:
         assert p["grid"] <= CU                               # one row strip per CU at most
 
 
 def test_policy_shapes_of_the_workloads(rn):
-    assert rn.rn_query_policy(0, 8192, 4096, 1, 1, CU)["lpr"] == 64                 # one row per wavefront
+    f = rn.rn_query_policy(0, 8192, 4096, 1, 1, CU)
+    assert f["lpr"] == 128 and f["nv"] == 4 and f["grid"] == 1024 and f["flags"] & 3 == 3
     b = rn.rn_query_policy(1, 8192, 4096, 1, 1, CU)
     assert b["nv"] == 1 and b["lpr"] == 512 and b["grid"] == 256
-    f = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
-    assert f["lpr"] == 128 and f["nv"] == 7
+    q = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
+    assert q["lpr"] == 256 and q["nv"] == 4 and q["grid"] == 512
 
 
 def test_policy_rejects_out_of_range(rn):
@@ -170,7 +179,8 @@ def test_bwd_validation(rn):
     assert call(lddx=100) == 5
     assert call(dx=A + 64) == 7                    # dx overlaps dy
     assert call(dw=A + 64) == 7                    # dw inside dy
-    assert call(ws=None) == 6                      # deterministic without a workspace
+    assert call(ws=None) == 6                      # no workspace
+    assert call(ws=None, det=0) == 6
     assert call(ws=C + 0x200008) == 4
 
 

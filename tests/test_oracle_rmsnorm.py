@@ -2,7 +2,7 @@
 not against itself:
 
 * hand-derived worked examples (tests/golden/hand_examples.json);
-* closed forms: constant rows normalise to sign(c)*w (the spec invariant),
+* closed forms: constant rows normalise to sign(c)*w,
   H = 1 forward and backward in closed form;
 * invariants: scale invariance at eps = 0, sum_j (y_j/w_j)^2 = H*ms/(ms+eps),
   sum_j dx_j*x_j = eps*rstd^3*sum_j g_j*w_j*x_j;

@@ -75,16 +75,16 @@ def generate(wl: Workload):
     return out
 
 
-# The five parity workloads and the benchmark shape of the fused producer.
+# The parity workloads at full size (the benchmark shape of the fused producer last).
 CONFIGS = {
-    "c1_f32_T64_H256": Workload("c1_f32_T64_H256", 64, 256, "f32", "f32", seed=SEED_BASE + 100),
-    "c2_bf16_T8192_H4096": Workload("c2_bf16_T8192_H4096", 8192, 4096, "bf16", "bf16", seed=SEED_BASE + 200),
-    "c3_bf16_T58497_H2048_outliers": Workload("c3_bf16_T58497_H2048_outliers", 58497, 2048, "bf16", "f32",
+    "f32_T64_H256": Workload("f32_T64_H256", 64, 256, "f32", "f32", seed=SEED_BASE + 100),
+    "bf16_T8192_H4096": Workload("bf16_T8192_H4096", 8192, 4096, "bf16", "bf16", seed=SEED_BASE + 200),
+    "bf16_T58497_H2048_outliers_f32w": Workload("bf16_T58497_H2048_outliers_f32w", 58497, 2048, "bf16", "f32",
                                               x_std=2.0, outlier_frac=0.01, outlier_scale=50.0,
                                               seed=SEED_BASE + 300),
-    "c4_fp8_T4096_H7168": Workload("c4_fp8_T4096_H7168", 4096, 7168, "bf16", "bf16", residual=True,
+    "fp8_T4096_H7168": Workload("fp8_T4096_H7168", 4096, 7168, "bf16", "bf16", residual=True,
                                    seed=SEED_BASE + 400),
-    "c5_bf16_T65536_H5120": Workload("c5_bf16_T65536_H5120", 65536, 5120, "bf16", "f32", seed=SEED_BASE + 500),
+    "bf16_T65536_H5120_f32w": Workload("bf16_T65536_H5120_f32w", 65536, 5120, "bf16", "f32", seed=SEED_BASE + 500),
     "fp8_T8192_H4096": Workload("fp8_T8192_H4096", 8192, 4096, "bf16", "bf16", residual=True,
                                 seed=SEED_BASE + 600),
 }
