@@ -33,6 +33,13 @@
 
 namespace rn {
 
+// Workspace layout: column blocks of RN_PART_COLS columns; block b holds the
+// G strip partials of its columns contiguously, [b][strip][column % 16].
+__device__ __forceinline__ int64_t part_index(int64_t col, int64_t strip, int64_t G)
+{
+    return ((col / RN_PART_COLS) * G + strip) * RN_PART_COLS + (col % RN_PART_COLS);
+}
+
 template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 {
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 #pragma unroll
         for (int k = 0; k < WCH; ++k) {
             u32x4 t = wr[i][k];
-            opaque(t);
+            if constexpr (NV > 1) opaque(t);     // one vector per lane: keep w unpacked
             unpack<WT>(t, wf + k * WPER);
         }
     };
@@ -118,6 +125,10 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         const int64_t r = W.row(it);
         const bool valid = W.valid(r);
         const float rs = valid ? b.rs : 0.0f;
+        // With one vector per lane the unpacked row (g, x, g*w) stays in
+        // registers between the two passes; wider lanes unpack it again.
+        constexpr bool KEEP = (NV == 1);
+        float gk[KEEP ? NV : 1][E], xk[KEEP ? NV : 1][E], gwk[KEEP ? NV : 1][E];
         // s = sum_j g*w*x (the row's dot product is rstd * s), and the exact
         // dw contributions of this row.
         const double rsd = (double)rs;
@@ -130,11 +141,17 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
             w_of(i, wf);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                sgwx = __builtin_fmaf(g[e] * wf[e], x[e], sgwx);
+                const float gw = g[e] * wf[e];
+                sgwx = __builtin_fmaf(gw, x[e], sgwx);
                 if constexpr (XT == DT_BF16)
                     acc[i][e] = __builtin_fma((double)(g[e] * x[e]), rsd, acc[i][e]);
                 else
                     acc[i][e] = __builtin_fma((double)g[e] * (double)x[e], rsd, acc[i][e]);
+                if constexpr (KEEP) {
+                    xk[i][e] = x[e];
+                    gwk[i][e] = gw;
+                    (void)gk;
+                }
             }
         }
         sgwx = R.sum(sgwx, red, it);
@@ -146,15 +163,21 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
             u32x4* dxrow = reinterpret_cast<u32x4*>(dxbase + r * a.lddx * XB);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                float g[E], x[E], wf[E], o[E];
-                u32x4 gc = b.g[i], xc = b.x[i];
-                opaque(gc);
-                opaque(xc);
-                unpack<XT>(gc, g);
-                unpack<XT>(xc, x);
-                w_of(i, wf);
+                float o[E];
+                if constexpr (KEEP) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(rs, g[e] * wf[e], -k2 * x[e]);
+                    for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(rs, gwk[i][e], -k2 * xk[i][e]);
+                } else {
+                    float g[E], x[E], wf[E];
+                    u32x4 gc = b.g[i], xc = b.x[i];
+                    opaque(gc);
+                    opaque(xc);
+                    unpack<XT>(gc, g);
+                    unpack<XT>(xc, x);
+                    w_of(i, wf);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(rs, g[e] * wf[e], -k2 * x[e]);
+                }
                 if (cok[i]) st16<NT>(dxrow + cix[i], pack<XT>(o));
             }
         }
@@ -177,7 +200,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                 for (int e = 0; e < E; ++e) {
                     const float p = (float)acc[i][e];
                     const int64_t col = (int64_t)c * E + e;
-                    part[strip * a.H + col] = p;
+                    part[part_index(col, strip, G)] = p;
                 }
             }
         }
@@ -198,7 +221,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                     for (int q = 0; q < gpw; ++q) s += stage[(q * lpr + l) * HALF + e];
                     const float p = (float)s;
                     const int64_t col = (int64_t)c * E + h0 + e;
-                    part[strip * a.H + col] = p;
+                    part[part_index(col, strip, G)] = p;
                 }
             }
             __syncthreads();
@@ -206,30 +229,29 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     }
 }
 
-// dw[j] = fp32( sum over g = 0..G-1 of part[g][j] ), FP64, fixed order: the 16
-// wavefronts of a work-group sum contiguous ranges of g in order, then the 16
-// range sums are added in wavefront order.  One lane per column.
-__global__ __launch_bounds__(1024) void k_dw_reduce(ReduceArgs a)
+// dw[j] = fp32( sum over g = 0..G-1 of the strip partials of column j ), in
+// FP64 and a fixed order.  One work-group per block of 16 columns, whose G x 16
+// partials are contiguous.  Thread t owns column t % 16 and the strips
+// g = t/16, t/16 + 16, t/16 + 32, ... (summed in that order); the 16 sums of a
+// column are then added in the order t/16 = 0, 1, ..., 15.
+__global__ __launch_bounds__(256) void k_dw_reduce(ReduceArgs a)
 {
-    constexpr int NW = 16;
-    __shared__ double red[NW][64];
-    const int wv = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int64_t col = (int64_t)blockIdx.x * 64 + lane;
-    const int64_t g0 = (wv * a.G) / NW, g1 = ((wv + 1) * a.G) / NW;
+    __shared__ double red[16][16];
+    const int t = threadIdx.x;
+    const int c = t & 15, q = t >> 4;
+    const int64_t blk = blockIdx.x;
+    const float* p = a.part + blk * a.G * RN_PART_COLS;
     double s = 0.0;
-    if (col < a.H) {
-        const float* p = a.part + col;
-#pragma unroll 8
-        for (int64_t g = g0; g < g1; ++g) s += (double)p[g * a.H];
-    }
-    red[wv][lane] = s;
+#pragma unroll 4
+    for (int64_t g = q; g < a.G; g += 16) s += (double)p[g * RN_PART_COLS + c];
+    red[q][c] = s;
     __syncthreads();
-    if (wv == 0 && col < a.H) {
-        double t = 0.0;
+    const int64_t col = blk * RN_PART_COLS + t;
+    if (t < 16 && col < a.H) {
+        double u = 0.0;
 #pragma unroll
-        for (int k = 0; k < NW; ++k) t += red[k][lane];
-        a.dw[col] = (float)t;
+        for (int k = 0; k < 16; ++k) u += red[k][t];
+        a.dw[col] = (float)u;
     }
 }
 
@@ -297,8 +319,8 @@ hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, const Policy& 
 
 hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s)
 {
-    const unsigned grid = (unsigned)((a.H + 63) / 64);
-    hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(1024), 0, s, a);
+    const unsigned grid = (unsigned)((a.H + RN_PART_COLS - 1) / RN_PART_COLS);
+    hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -253,6 +253,13 @@ int check_h(int64_t H, int dt)
     return RN_OK;
 }
 
+// Workspace bytes for G row strips: fp32 partials in blocks of 16 columns.
+size_t workspace_need(int64_t G, int64_t H)
+{
+    const int64_t cols = (H + rn::RN_PART_COLS - 1) / rn::RN_PART_COLS * rn::RN_PART_COLS;
+    return (size_t)G * (size_t)cols * sizeof(float);
+}
+
 // Clear a stale error left by earlier HIP calls on this thread, so that the
 // error read after our launch is our own.
 void clear_last_error() { (void)hipGetLastError(); }
@@ -317,7 +324,7 @@ size_t rn_bwd_workspace_bytes_for(int64_t T, int64_t H, int cu_count)
     for (int dt = 0; dt < 2; ++dt) {
         if (H % elems_per_chunk(dt) != 0) continue;
         if (policy_bwd(T, H, dt, cu_count, &p) != RN_OK) continue;
-        const size_t b = (size_t)p.grid * (size_t)H * sizeof(float);
+        const size_t b = workspace_need(p.grid, H);
         if (b > best) best = b;
     }
     if (best == 0) return (size_t)-1;
@@ -408,7 +415,7 @@ int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_
         return RN_OK;
     }
     if ((st = policy_bwd(T, H, x_dtype, cu, &p)) != RN_OK) return st;
-    const size_t need = (size_t)p.grid * (size_t)H * sizeof(float);
+    const size_t need = workspace_need(p.grid, H);
     if (workspace_bytes < need) return RN_ERR_WORKSPACE;
     {
         const Extent ews = vec_extent(workspace, (int64_t)(need / 4), 4);

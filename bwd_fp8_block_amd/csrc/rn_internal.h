@@ -41,13 +41,16 @@ struct BwdArgs {
     const void* w;
     const float* rstd;
     void* dx; int64_t lddx;
-    float* part;                 // workspace [grid][H]: one fp32 dw partial per row strip
+    float* part;                 // workspace: one fp32 dw partial per (row strip, column)
     int64_t T; int H; int nch;
     float inv_h;                 // 1/H rounded to fp32
 };
 
+// dw partials are stored in blocks of this many columns (see rn_bwd.hip).
+constexpr int RN_PART_COLS = 16;
+
 struct ReduceArgs {
-    const float* part;           // [G][H]
+    const float* part;           // [ceil(H/16)][G][16]
     float* dw;                   // [H]
     int64_t G; int H;
 };

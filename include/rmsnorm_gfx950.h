@@ -101,7 +101,8 @@ int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype,
 
 /*
  * Size in bytes of the workspace that rmsnorm_bwd needs for (T, H) on HIP
- * device `device` (fp32 partial sums, one row of H per row strip).  The value never decreases with T, so a workspace sized for the
+ * device `device` (fp32 partial sums: one per row strip and column, H
+ * rounded up to a multiple of 16).  The value never decreases with T, so a workspace sized for the
  * largest T can be reused for every smaller T.  Returns 0 for T == 0 and
  * (size_t)-1 on invalid arguments or when the device cannot be queried.
  */
