@@ -64,6 +64,12 @@ def _load():
     lib.rno_add_rmsnorm_fp8.argtypes = [vp, i64, vp, i64, vp, i64, i64, f32,
                                         vp, i64, vp, vp, i64, vp, i64, vp, i64, vp, i64]
     lib.rno_add_rmsnorm_fp8.restype = i32
+    lib.rno_residual_add.argtypes = [vp, i64, vp, i64, i32, i64, i64, vp, i64]
+    lib.rno_residual_add.restype = i32
+    lib.rno_rmsnorm_fwd_residual.argtypes = [vp, i64, vp, i64, i32, vp, i32, i64, i64, f32, vp, i64, vp, i64, vp]
+    lib.rno_rmsnorm_fwd_residual.restype = i32
+    lib.rno_rmsnorm_bwd_residual.argtypes = [vp, i64, vp, i64, i32, vp, i32, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.rno_rmsnorm_bwd_residual.restype = i32
     _lib = lib
     return lib
 
@@ -185,3 +191,51 @@ def add_rmsnorm_fp8(x: np.ndarray, res: np.ndarray, w: np.ndarray, eps: float,
     if rc:
         raise ValueError("oracle add_rmsnorm_fp8 rejected the arguments (%d)" % rc)
     return dict(h=h, rstd=rstd, normed=normed, normed_bf16=nb, scale=scale, codes=codes)
+
+
+def residual_add(x: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = x + u rounded once into x's dtype (uint16 bf16 bits or float32)."""
+    lib = _load()
+    assert x.dtype == u.dtype and x.shape == u.shape
+    T, H = x.shape
+    h = np.empty((T, H), dtype=x.dtype)
+    rc = lib.rno_residual_add(_ptr(x), _row_stride(x) if T else H, _ptr(u), _row_stride(u) if T else H,
+                              _dtype_code(x), T, H, _ptr(h), H)
+    if rc:
+        raise ValueError("oracle residual_add rejected the arguments (%d)" % rc)
+    return h
+
+
+def rmsnorm_fwd_residual(x: np.ndarray, u: np.ndarray, w: np.ndarray, eps: float, want_y: bool = True):
+    """Training forward with a residual: returns (y unrounded float64 or None, rstd float64 [T],
+    h_new [T,H] in x's dtype)."""
+    lib = _load()
+    assert x.dtype == u.dtype and x.shape == u.shape
+    T, H = x.shape
+    h = np.empty((T, H), dtype=x.dtype)
+    y = np.empty((T, H), dtype=np.float64) if want_y else None
+    rstd = np.empty((T,), dtype=np.float64)
+    rc = lib.rno_rmsnorm_fwd_residual(_ptr(x), _row_stride(x) if T else H, _ptr(u), _row_stride(u) if T else H,
+                                      _dtype_code(x), _ptr(w), _dtype_code(w), T, H, np.float32(eps),
+                                      _ptr(h), H, _ptr(y), H, _ptr(rstd))
+    if rc:
+        raise ValueError("oracle rmsnorm_fwd_residual rejected the arguments (%d)" % rc)
+    return y, rstd, h
+
+
+def rmsnorm_bwd_residual(dy: np.ndarray, h: np.ndarray, w: np.ndarray, rstd: np.ndarray, g_res: np.ndarray,
+                         want_dx: bool = True, want_dw: bool = True):
+    """Training backward with a residual-stream gradient: returns (dx_total = dx + g_res unrounded
+    float64 or None, dw float64 or None)."""
+    lib = _load()
+    assert dy.dtype == h.dtype == g_res.dtype and dy.shape == h.shape == g_res.shape
+    T, H = h.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+    dx = np.empty((T, H), dtype=np.float64) if want_dx else None
+    dw = np.empty((H,), dtype=np.float64) if want_dw else None
+    rc = lib.rno_rmsnorm_bwd_residual(_ptr(dy), _row_stride(dy) if T else H, _ptr(h), _row_stride(h) if T else H,
+                                      _dtype_code(h), _ptr(w), _dtype_code(w), _ptr(rstd),
+                                      _ptr(g_res), _row_stride(g_res) if T else H, T, H, _ptr(dx), H, _ptr(dw))
+    if rc:
+        raise ValueError("oracle rmsnorm_bwd_residual rejected the arguments (%d)" % rc)
+    return dx, dw

@@ -43,6 +43,11 @@
  *      (a negative value that rounds to zero is 0x80).
  *  R7  scale layout: element (row m, block k) lives at scale[k*scale_ld + m];
  *      padding rows m in [T, scale_ld) are not written.
+ *  R11 the training forward with a residual stores h_new = x + u rounded once
+ *      into the dtype of x (bf16 or fp32) and normalises that rounded h_new.
+ *  R12 the training backward with a residual-stream gradient returns
+ *      dx_total = dx + g_residual, the sum taken before the one rounding
+ *      into the output dtype; dw is unchanged by g_residual.
  */
 #include <math.h>
 #include <stddef.h>
@@ -340,5 +345,67 @@ int rno_add_rmsnorm_fp8(const uint16_t* x, int64_t ldx,
             if (rc) return rc;
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Training pair with a residual stream.                                     */
+/* Cake commit #5741, API and Design: the forward optionally takes a         */
+/* residual u, returns h_new = bf16(x + u) and normalises it; the backward   */
+/* of that forward adds the gradient arriving along the residual stream,     */
+/* g_residual, into the dx it returns (dx_total), so both inputs of the add  */
+/* receive the same gradient.  Readings R11, R12 (fp32 inputs: the same with */
+/* fp32 in place of bf16).                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* h = x + u, the exact sum rounded once into x's dtype. */
+int rno_residual_add(const void* x, int64_t ldx, const void* u, int64_t ldu, int dtype,
+                     int64_t T, int64_t H, void* h, int64_t ldh)
+{
+    if (T < 0 || H <= 0) return 1;
+    for (int64_t r = 0; r < T; ++r) {
+        for (int64_t j = 0; j < H; ++j) {
+            double s = load_elem(x, dtype, r * ldx + j) + load_elem(u, dtype, r * ldu + j);
+            if (dtype == RNO_BF16)
+                ((uint16_t*)h)[r * ldh + j] = rno_double_to_bf16(s);
+            else
+                ((float*)h)[r * ldh + j] = (float)s;      /* one round-to-nearest-even */
+        }
+    }
+    return 0;
+}
+
+/* y, rstd of RMSNorm applied to h_new = round(x + u); h_new is written to h
+ * (required, x's dtype, row stride ldh). */
+int rno_rmsnorm_fwd_residual(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dtype,
+                             const void* w, int w_dtype,
+                             int64_t T, int64_t H, float eps,
+                             void* h, int64_t ldh,
+                             double* y, int64_t ldy,      /* may be NULL */
+                             double* rstd)                /* may be NULL */
+{
+    if (!h) return 1;
+    int rc = rno_residual_add(x, ldx, u, ldu, x_dtype, T, H, h, ldh);
+    if (rc) return rc;
+    return rno_rmsnorm_fwd(h, ldh, x_dtype, w, w_dtype, T, H, eps, y, ldy, rstd);
+}
+
+/* dx_total = dx + g_residual (unrounded) and dw, at the forward's h_new and
+ * stored rstd. */
+int rno_rmsnorm_bwd_residual(const void* dy, int64_t lddy,
+                             const void* h, int64_t ldh, int x_dtype,
+                             const void* w, int w_dtype,
+                             const double* rstd,
+                             const void* g_res, int64_t ldgr,
+                             int64_t T, int64_t H,
+                             double* dx, int64_t lddx,    /* may be NULL */
+                             double* dw)                  /* may be NULL */
+{
+    int rc = rno_rmsnorm_bwd(dy, lddy, h, ldh, x_dtype, w, w_dtype, rstd, T, H, dx, lddx, dw);
+    if (rc) return rc;
+    if (dx)
+        for (int64_t r = 0; r < T; ++r)
+            for (int64_t j = 0; j < H; ++j)
+                dx[r * lddx + j] += load_elem(g_res, x_dtype, r * ldgr + j);
     return 0;
 }
