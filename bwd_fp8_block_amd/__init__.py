@@ -1,5 +1,6 @@
-"""MI355X (gfx950) RMSNorm: forward, fused dX+dW backward, and the fused
-residual-add + RMSNorm + FP8 e4m3 1x128 block-quant producer.
+"""MI355X (gfx950) RMSNorm: forward, fused dX+dW backward, the fused
+residual-add + RMSNorm + FP8 e4m3 1x128 block-quant producer, and the
+training pair with a residual stream.
 
 Thin ctypes binding over ``librmsnorm_gfx950.so``, whose C ABI is declared in
 ``include/rmsnorm_gfx950.h``.  Each function here only marshals arguments:
@@ -23,6 +24,7 @@ __all__ = [
     "rn_query_policy", "rn_bwd_workspace_bytes_for", "rn_status_string", "rn_version",
     "rn_selftest_quant", "rn_selftest_cvt_e4m3",
     "plan_rmsnorm_fwd", "plan_rmsnorm_bwd", "plan_add_rmsnorm_fp8_block_quant",
+    "rmsnorm_fwd_residual", "rmsnorm_bwd_residual", "plan_rmsnorm_fwd_residual", "plan_rmsnorm_bwd_residual",
 ]
 
 RN_F32 = 0
@@ -55,6 +57,12 @@ lib.rmsnorm_bwd.restype = _i32
 lib.add_rmsnorm_fp8_block_quant.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64,
                                             _i64, _i64, _f32, _vp]
 lib.add_rmsnorm_fp8_block_quant.restype = _i32
+lib.rmsnorm_fwd_residual.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp, _i64, _vp, _i64, _vp,
+                                     _i64, _i64, _f32, _vp]
+lib.rmsnorm_fwd_residual.restype = _i32
+lib.rmsnorm_bwd_residual.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp,
+                                     _i64, _i64, _i32, _vp, _sz, _vp]
+lib.rmsnorm_bwd_residual.restype = _i32
 lib.rn_query_policy.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.rn_query_policy.restype = _i32
 lib.rn_bwd_workspace_bytes_for.argtypes = [_i64, _i64, _i32]
@@ -249,6 +257,54 @@ def _prep_fp8(x, residual, w, out, block_scale, normed_out, eps):
     return dev, lib.add_rmsnorm_fp8_block_quant, args
 
 
+def _prep_fwd_residual(x, u, w, y, h_out, rstd, eps):
+    dev = _dev((x, u, w, y, h_out, rstd))
+    T, H = x.shape
+    for t in (u, y, h_out):
+        if t.shape != x.shape or t.dtype != x.dtype:
+            raise ValueError("rmsnorm_fwd_residual: u, y and h_out must match x in shape and dtype")
+    if w.shape != (H,) or rstd.shape != (T,) or rstd.dtype != torch.float32:
+        raise ValueError("rmsnorm_fwd_residual: w/rstd shape or dtype mismatch")
+    px, ldx = _mat(x, "x")
+    pu, ldu = _mat(u, "u")
+    py, ldy = _mat(y, "y")
+    ph, ldh = _mat(h_out, "h_out")
+    with _on(dev):
+        args = (px, ldx, pu, ldu, _dt(x), _vec(w, "w"), _dt(w), py, ldy, ph, ldh, _vec(rstd, "rstd"),
+                T, H, float(eps), _stream(dev))
+    return dev, lib.rmsnorm_fwd_residual, args
+
+
+def rmsnorm_fwd_residual(x: torch.Tensor, u: torch.Tensor, w: torch.Tensor, y: torch.Tensor,
+                         h_out: torch.Tensor, rstd: torch.Tensor, eps: float) -> None:
+    """h_out = round(x + u); y = h_out * rstd * w with rstd = 1/sqrt(mean(h_out^2) + eps).
+    h_out may be x or u itself (in-place update of the residual stream)."""
+    dev, fn, args = _prep_fwd_residual(x, u, w, y, h_out, rstd, eps)
+    with _on(dev):
+        st = fn(*args)
+    _check("rmsnorm_fwd_residual", st)
+
+
+def _prep_bwd_residual(dy, x, w, rstd, g_residual, dx, dw, deterministic, workspace):
+    dev, _, a = _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, workspace)
+    if g_residual.shape != x.shape or g_residual.dtype != x.dtype or g_residual.device != dev:
+        raise ValueError("rmsnorm_bwd_residual: g_residual must match x in shape, dtype and device")
+    pg, ldg = _mat(g_residual, "g_residual")
+    args = a[:8] + (pg, ldg) + a[8:]
+    return dev, lib.rmsnorm_bwd_residual, args
+
+
+def rmsnorm_bwd_residual(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor,
+                         g_residual: torch.Tensor, dx: torch.Tensor, dw: torch.Tensor,
+                         deterministic: bool = True, workspace: torch.Tensor | None = None) -> None:
+    """Backward of rmsnorm_fwd_residual: dx = (the rmsnorm_bwd dx at x = h_out) + g_residual,
+    dw as in rmsnorm_bwd.  g_residual may be dx itself (in-place accumulation)."""
+    dev, fn, args = _prep_bwd_residual(dy, x, w, rstd, g_residual, dx, dw, deterministic, workspace)
+    with _on(dev):
+        st = fn(*args)
+    _check("rmsnorm_bwd_residual", st)
+
+
 def _plan(name, prep):
     dev, fn, args = prep
     cur = torch.cuda.current_device
@@ -276,6 +332,17 @@ def plan_rmsnorm_bwd(dy, x, w, rstd, dx, dw, deterministic=True, workspace=None)
 def plan_add_rmsnorm_fp8_block_quant(x, residual, w, out, block_scale, normed_out, eps):
     """Planned add_rmsnorm_fp8_block_quant (see plan_rmsnorm_fwd)."""
     return _plan("add_rmsnorm_fp8_block_quant", _prep_fp8(x, residual, w, out, block_scale, normed_out, eps))
+
+
+def plan_rmsnorm_fwd_residual(x, u, w, y, h_out, rstd, eps):
+    """Planned rmsnorm_fwd_residual (see plan_rmsnorm_fwd)."""
+    return _plan("rmsnorm_fwd_residual", _prep_fwd_residual(x, u, w, y, h_out, rstd, eps))
+
+
+def plan_rmsnorm_bwd_residual(dy, x, w, rstd, g_residual, dx, dw, deterministic=True, workspace=None):
+    """Planned rmsnorm_bwd_residual (see plan_rmsnorm_fwd)."""
+    return _plan("rmsnorm_bwd_residual",
+                 _prep_bwd_residual(dy, x, w, rstd, g_residual, dx, dw, deterministic, workspace))
 
 
 def rn_query_policy(op: int, T: int, H: int, x_dtype: int, w_dtype: int, cu_count: int) -> dict:

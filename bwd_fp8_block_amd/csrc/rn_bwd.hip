@@ -28,6 +28,10 @@
 // Adding the strip partials with fp32 atomics instead was measured over the
 // per-element dw budget at T = 65536, H = 5120 (1.03x), and was not faster
 // than this second kernel, so both modes of the entry point use this path.
+//
+// Residual form (RES; [C] API and Design: Backward, the training backward
+// with a residual): the gradient arriving along the residual stream is added
+// to dx in fp32 before the one rounding into x's dtype; dw is unchanged.
 #include "rn_device.h"
 #include "rn_internal.h"
 
@@ -40,7 +44,7 @@ __device__ __forceinline__ int64_t part_index(int64_t col, int64_t strip, int64_
     return ((col / RN_PART_COLS) * G + strip) * RN_PART_COLS + (col % RN_PART_COLS);
 }
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, bool RES>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -97,10 +101,12 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 
     const char* gbase = static_cast<const char*>(a.dy);
     const char* xbase = static_cast<const char*>(a.x);
+    const char* grbase = static_cast<const char*>(a.gres);
     char* dxbase = static_cast<char*>(a.dx);
 
     struct RowBuf {
         u32x4 g[NV], x[NV];
+        u32x4 gr[RES ? NV : 1];
         float rs;
     };
 
@@ -119,6 +125,11 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
             b.g[i] = ld16<NT>(grow + cix[i]);
             b.x[i] = ld16<NT>(xrow + cix[i]);
         }
+        if constexpr (RES) {
+            const u32x4* rrow = reinterpret_cast<const u32x4*>(grbase + rr * a.ldgr * XB);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) b.gr[i] = ld16<NT>(rrow + cix[i]);
+        }
     };
 
     auto process = [&](const RowBuf& b, int it) {
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         // With one vector per lane the unpacked row (g, x, g*w) stays in
         // registers between the two passes; wider lanes unpack it again.
         constexpr bool KEEP = (NV == 1);
-        float gk[KEEP ? NV : 1][E], xk[KEEP ? NV : 1][E], gwk[KEEP ? NV : 1][E];
+        float xk[KEEP ? NV : 1][E], gwk[KEEP ? NV : 1][E];
         // s = sum_j g*w*x (the row's dot product is rstd * s), and the exact
         // dw contributions of this row.
         const double rsd = (double)rs;
@@ -150,7 +161,6 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                 if constexpr (KEEP) {
                     xk[i][e] = x[e];
                     gwk[i][e] = gw;
-                    (void)gk;
                 }
             }
         }
@@ -177,6 +187,12 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                     w_of(i, wf);
 #pragma unroll
                     for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(rs, g[e] * wf[e], -k2 * x[e]);
+                }
+                if constexpr (RES) {
+                    float gr[E];
+                    unpack<XT>(b.gr[i], gr);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) o[e] += gr[e];
                 }
                 if (cok[i]) st16<NT>(dxrow + cix[i], pack<XT>(o));
             }
@@ -264,27 +280,28 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t n)
 // ---------------------------------------------------------------------------
 // Variant table and dispatch.
 // ---------------------------------------------------------------------------
-template <int XT, int WT, int LPRC, int NV, int WGMAX>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool RES>
 static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
 {
     const dim3 g((unsigned)p.grid), b(p.wgs);
     const int pd = (p.flags >> 4) & 7;
-    const bool nt = (p.flags & RN_FLAG_NT) != 0;
+    // The residual form is compiled with streaming accesses only.
+    const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
     if constexpr (LPRC == 64 && NV == 1) {
         // the main variant: pipeline depth is a launch choice
         if (pd == 3) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3>), g, b, 0, s, a);
-            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3>), g, b, 0, s, a);
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3, RES>), g, b, 0, s, a);
+            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3, false>), g, b, 0, s, a);
             return hipGetLastError();
         }
         if (pd == 4) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4>), g, b, 0, s, a);
-            else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4>), g, b, 0, s, a);
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4, RES>), g, b, 0, s, a);
+            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4, false>), g, b, 0, s, a);
             return hipGetLastError();
         }
     }
-    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 2>), g, b, 0, s, a);
+    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2, RES>), g, b, 0, s, a);
+    else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 2, false>), g, b, 0, s, a);
     return hipGetLastError();
 }
 
@@ -299,22 +316,28 @@ bool bwd_variant_exists(int lprc, int nv, int wgs)
     return false;
 }
 
-template <int XT, int WT>
+template <int XT, int WT, bool RES>
 static hipError_t bwd_dispatch(const BwdArgs& a, const Policy& p, hipStream_t s)
 {
     const int lprc = p.lpr < 64 ? p.lpr : 64;
-#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return bwd_go<XT, WT, C, N, W>(a, p, s);
+#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return bwd_go<XT, WT, C, N, W, RES>(a, p, s);
     RN_BWD_VARIANTS(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s)
+template <bool RES>
+static hipError_t bwd_dtypes(const BwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s)
 {
-    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16>(a, p, s);
-    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32>(a, p, s);
-    if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return bwd_dispatch<DT_BF16, DT_BF16, RES>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return bwd_dispatch<DT_BF16, DT_F32, RES>(a, p, s);
+    if (x_dtype == DT_F32 && w_dtype == DT_F32) return bwd_dispatch<DT_F32, DT_F32, RES>(a, p, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s)
+{
+    return residual ? bwd_dtypes<true>(a, x_dtype, w_dtype, p, s) : bwd_dtypes<false>(a, x_dtype, w_dtype, p, s);
 }
 
 hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s)

@@ -16,12 +16,16 @@
 // Loads are never predicated: out-of-range chunks and rows load from a
 // clamped in-bounds address and are zeroed, which keeps the loads in one
 // unbranched batch.  NT selects non-temporal (streaming) loads and stores.
+//
+// Residual form (RES; [C] API and Design: Forward, the training forward with
+// a residual): the row read is h_new = x + u, added in fp32 and rounded once
+// to x's dtype, stored, and normalised in place of x.
 #include "rn_device.h"
 #include "rn_internal.h"
 
 namespace rn {
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, bool RES>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -60,7 +64,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     }
 
     const char* xbase = static_cast<const char*>(a.x);
+    const char* ubase = static_cast<const char*>(a.u);
     char* ybase = static_cast<char*>(a.y);
+    char* hbase = static_cast<char*>(a.h);
 
     // Rows of this group: lo + grp + it * gpw.  Past the end of the chunk the
     // address is clamped to the chunk's last row (nothing is stored for it).
@@ -68,15 +74,36 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     // the next row stay in flight while the current row is processed.
     struct RowBuf {
         u32x4 v[NV];
+        u32x4 u[RES ? NV : 1];
     };
     auto load = [&](RowBuf& b, int it) {
-        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + W.clamp(W.row(it)) * a.ldx * XB);
+        const int64_t rr = W.clamp(W.row(it));
+        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * XB);
 #pragma unroll
         for (int i = 0; i < NV; ++i) b.v[i] = ld16<NT>(row + cix[i]);
+        if constexpr (RES) {
+            const u32x4* urow = reinterpret_cast<const u32x4*>(ubase + rr * a.ldu * XB);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) b.u[i] = ld16<NT>(urow + cix[i]);
+        }
     };
 
     auto process = [&](const RowBuf& b, int it) {
-        const u32x4 (&xv)[NV] = b.v;
+        // The row that is normalised: x, or h_new = round(x + u).
+        u32x4 xv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if constexpr (RES) {
+                float f[E], g[E];
+                unpack<XT>(b.v[i], f);
+                unpack<XT>(b.u[i], g);
+#pragma unroll
+                for (int e = 0; e < E; ++e) f[e] += g[e];
+                xv[i] = pack<XT>(f);
+            } else {
+                xv[i] = b.v[i];
+            }
+        }
         const int64_t r = W.row(it);
         const bool valid = W.valid(r);
         float ss = 0.0f;
@@ -92,6 +119,12 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
         const float rs = 1.0f / __builtin_sqrtf(ms + a.eps);
         if (valid) {
             u32x4* yrow = reinterpret_cast<u32x4*>(ybase + r * a.ldy * XB);
+            if constexpr (RES) {
+                u32x4* hrow = reinterpret_cast<u32x4*>(hbase + r * a.ldh * XB);
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (cok[i]) st16<NT>(hrow + cix[i], xv[i]);
+            }
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 float f[E], wf[E], o[E];
@@ -120,21 +153,22 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 // Variant table and dispatch: template on the group class (16, 32, 64+) and
 // on the vectors per lane; the group width for class 64 is a launch argument.
 // ---------------------------------------------------------------------------
-template <int XT, int WT, int LPRC, int NV, int WGMAX>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool RES>
 static hipError_t fwd_go(const FwdArgs& a, const Policy& p, hipStream_t s)
 {
     const dim3 g((unsigned)p.grid), b(p.wgs);
-    const bool nt = (p.flags & RN_FLAG_NT) != 0;
+    // The residual form is compiled with streaming accesses only.
+    const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
     if constexpr (NV <= 4) {
         // short per-lane rows: a third row buffer is affordable
         if (((p.flags >> 4) & 7) == 3) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 3>), g, b, 0, s, a);
-            else hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 3>), g, b, 0, s, a);
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 3, RES>), g, b, 0, s, a);
+            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 3, false>), g, b, 0, s, a);
             return hipGetLastError();
         }
     }
-    if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 2>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 2>), g, b, 0, s, a);
+    if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 2, RES>), g, b, 0, s, a);
+    else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 2, false>), g, b, 0, s, a);
     return hipGetLastError();
 }
 
@@ -151,22 +185,28 @@ bool fwd_variant_exists(int lprc, int nv, int wgs)
     return false;
 }
 
-template <int XT, int WT>
+template <int XT, int WT, bool RES>
 static hipError_t fwd_dispatch(const FwdArgs& a, const Policy& p, hipStream_t s)
 {
     const int lprc = p.lpr < 64 ? p.lpr : 64;
-#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return fwd_go<XT, WT, C, N, W>(a, p, s);
+#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return fwd_go<XT, WT, C, N, W, RES>(a, p, s);
     RN_FWD_VARIANTS(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s)
+template <bool RES>
+static hipError_t fwd_dtypes(const FwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s)
 {
-    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return fwd_dispatch<DT_BF16, DT_BF16>(a, p, s);
-    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return fwd_dispatch<DT_BF16, DT_F32>(a, p, s);
-    if (x_dtype == DT_F32 && w_dtype == DT_F32) return fwd_dispatch<DT_F32, DT_F32>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return fwd_dispatch<DT_BF16, DT_BF16, RES>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return fwd_dispatch<DT_BF16, DT_F32, RES>(a, p, s);
+    if (x_dtype == DT_F32 && w_dtype == DT_F32) return fwd_dispatch<DT_F32, DT_F32, RES>(a, p, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s)
+{
+    return residual ? fwd_dtypes<true>(a, x_dtype, w_dtype, p, s) : fwd_dtypes<false>(a, x_dtype, w_dtype, p, s);
 }
 
 } // namespace rn

@@ -102,7 +102,10 @@ int elem_bytes(int dt) { return dt == RN_BF16 ? 2 : 4; }
 // with at most 4-8 vectors of 16 bytes per lane, walked as one interleaved
 // window, run at 0.95-0.97 of a same-traffic streaming copy for H = 2048 ..
 // 5120.  Short rows use 16/32/64-lane groups; very long rows more wavefronts.
-int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
+// The residual form holds two input rows per buffer: at four vectors per lane
+// three 256-thread work-groups fit on a CU (one beyond eight vectors), and the
+// grid is one full wave of them.
+int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p, bool residual = false)
 {
     const int nch = (int)(H / elems_per_chunk(x_dtype));
     if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
@@ -115,7 +118,7 @@ int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     if (p->lpr > 512) return RN_ERR_SHAPE;
     p->wgs = wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
-    const int64_t per_cu = p->nv <= 4 ? 4 : 2;
+    const int64_t per_cu = p->nv <= 2 ? 4 : p->nv <= 4 ? (residual ? 3 : 4) : (residual ? 1 : 2);
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
@@ -264,6 +267,147 @@ size_t workspace_need(int64_t G, int64_t H)
 // error read after our launch is our own.
 void clear_last_error() { (void)hipGetLastError(); }
 
+// Same buffer, same row stride: an element-wise in-place update.
+bool same_matrix(const void* a, int64_t lda, const void* b, int64_t ldb) { return a == b && lda == ldb; }
+
+// Forward, plain or with a residual stream (u, h_out).
+int fwd_common(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dtype, const void* w, int w_dtype,
+               void* y, int64_t ldy, void* h, int64_t ldh, float* rstd, int64_t T, int64_t H, float eps,
+               void* stream, bool residual)
+{
+    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
+    int st;
+    if ((st = check_h(H, x_dtype)) != RN_OK) return st;
+    if (T < 0) return RN_ERR_SHAPE;
+    Policy p{};
+    if ((st = policy_fwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
+    if (T == 0) return RN_OK;
+    if (!x || !w || !y || !rstd) return RN_ERR_NULL;
+    if (residual && (!u || !h)) return RN_ERR_NULL;
+    if ((st = check_matrix(x, ldx, H, x_dtype)) != RN_OK) return st;
+    if ((st = check_matrix(y, ldy, H, x_dtype)) != RN_OK) return st;
+    if (residual) {
+        if ((st = check_matrix(u, ldu, H, x_dtype)) != RN_OK) return st;
+        if ((st = check_matrix(h, ldh, H, x_dtype)) != RN_OK) return st;
+    }
+    if (!aligned(w, 16) || !aligned(rstd, 4)) return RN_ERR_ALIGN;
+    const int xb = elem_bytes(x_dtype);
+    const Extent ex = mat_extent(x, T, H, ldx, xb), ey = mat_extent(y, T, H, ldy, xb);
+    const Extent ew = vec_extent(w, H, elem_bytes(w_dtype)), er = vec_extent(rstd, T, 4);
+    if (overlap(ey, ex) || overlap(ey, ew) || overlap(ey, er) || overlap(er, ex) || overlap(er, ew))
+        return RN_ERR_ALIAS;
+    if (residual) {
+        const Extent eu = mat_extent(u, T, H, ldu, xb), eh = mat_extent(h, T, H, ldh, xb);
+        if (overlap(ey, eu) || overlap(er, eu) || overlap(eh, ey) || overlap(eh, ew) || overlap(eh, er))
+            return RN_ERR_ALIAS;
+        if (overlap(eh, ex) && !same_matrix(h, ldh, x, ldx)) return RN_ERR_ALIAS;
+        if (overlap(eh, eu) && !same_matrix(h, ldh, u, ldu)) return RN_ERR_ALIAS;
+    }
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    if ((st = policy_fwd(T, H, x_dtype, cu, &p, residual)) != RN_OK) return st;
+    apply_override(0, T, (int)(H / elems_per_chunk(x_dtype)), &p);
+    log_policy(residual ? "fwd_residual" : "fwd", T, H, p);
+
+    rn::FwdArgs a{};
+    a.lpr = p.lpr;
+    a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0;
+    a.x = x; a.ldx = ldx;
+    a.u = u; a.ldu = ldu;
+    a.h = h; a.ldh = ldh;
+    a.w = w;
+    a.y = y; a.ldy = ldy;
+    a.rstd = rstd;
+    a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype)); a.eps = eps;
+    clear_last_error();
+    if (rn::launch_fwd(a, x_dtype, w_dtype, residual ? 1 : 0, p, (hipStream_t)stream) != hipSuccess)
+        return RN_ERR_LAUNCH;
+    return RN_OK;
+}
+
+// Backward, plain or with the residual-stream gradient g_residual.
+int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype,
+               const float* rstd, const void* gres, int64_t ldgr, void* dx, int64_t lddx, float* dw, int64_t T,
+               int64_t H, int deterministic, void* workspace, size_t workspace_bytes, void* stream, bool residual)
+{
+    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
+    int st;
+    if ((st = check_h(H, x_dtype)) != RN_OK) return st;
+    if (T < 0) return RN_ERR_SHAPE;
+    Policy p{};
+    if ((st = policy_bwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
+    if (!dw) return RN_ERR_NULL;
+    if (!aligned(dw, 4)) return RN_ERR_ALIGN;
+    const int xb = elem_bytes(x_dtype);
+    const Extent edw = vec_extent(dw, H, 4);
+    Extent edy{}, ex{}, edx{}, ew{}, er{}, eg{};
+    if (T > 0) {
+        if (!dy || !x || !w || !rstd || !dx) return RN_ERR_NULL;
+        if (residual && !gres) return RN_ERR_NULL;
+        if ((st = check_matrix(dy, lddy, H, x_dtype)) != RN_OK) return st;
+        if ((st = check_matrix(x, ldx, H, x_dtype)) != RN_OK) return st;
+        if ((st = check_matrix(dx, lddx, H, x_dtype)) != RN_OK) return st;
+        if (residual && (st = check_matrix(gres, ldgr, H, x_dtype)) != RN_OK) return st;
+        if (!aligned(w, 16) || !aligned(rstd, 4)) return RN_ERR_ALIGN;
+        edy = mat_extent(dy, T, H, lddy, xb);
+        ex = mat_extent(x, T, H, ldx, xb);
+        edx = mat_extent(dx, T, H, lddx, xb);
+        ew = vec_extent(w, H, elem_bytes(w_dtype));
+        er = vec_extent(rstd, T, 4);
+        if (overlap(edx, edy) || overlap(edx, ex) || overlap(edx, ew) || overlap(edx, er) || overlap(edx, edw) ||
+            overlap(edw, edy) || overlap(edw, ex) || overlap(edw, ew) || overlap(edw, er))
+            return RN_ERR_ALIAS;
+        if (residual) {
+            eg = mat_extent(gres, T, H, ldgr, xb);
+            if (overlap(edw, eg)) return RN_ERR_ALIAS;
+            if (overlap(edx, eg) && !same_matrix(dx, lddx, gres, ldgr)) return RN_ERR_ALIAS;
+        }
+        if (!workspace) return RN_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return RN_ERR_ALIGN;
+    }
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    clear_last_error();
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {
+        // No rows: the weight gradient is the empty sum.
+        if (rn::launch_fill_zero(dw, H, s) != hipSuccess) return RN_ERR_LAUNCH;
+        return RN_OK;
+    }
+    if ((st = policy_bwd(T, H, x_dtype, cu, &p)) != RN_OK) return st;
+    const size_t need = workspace_need(p.grid, H);
+    if (workspace_bytes < need) return RN_ERR_WORKSPACE;
+    {
+        const Extent ews = vec_extent(workspace, (int64_t)(need / 4), 4);
+        if (overlap(ews, edy) || overlap(ews, ex) || overlap(ews, ew) || overlap(ews, er) || overlap(ews, edx) ||
+            overlap(ews, edw) || (residual && overlap(ews, eg)))
+            return RN_ERR_ALIAS;
+    }
+    apply_override(1, T, (int)(H / elems_per_chunk(x_dtype)), &p);
+    log_policy(residual ? "bwd_residual" : "bwd", T, H, p);
+
+    rn::BwdArgs a{};
+    a.lpr = p.lpr;
+    a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0;
+    a.dy = dy; a.lddy = lddy;
+    a.x = x; a.ldx = ldx;
+    a.w = w;
+    a.rstd = rstd;
+    a.gres = gres; a.ldgr = ldgr;
+    a.dx = dx; a.lddx = lddx;
+    a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype));
+    a.inv_h = 1.0f / (float)H;
+    // Both modes run the same fixed-order reduction (see the header).
+    (void)deterministic;
+    a.part = static_cast<float*>(workspace);
+    if (rn::launch_bwd(a, x_dtype, w_dtype, residual ? 1 : 0, p, s) != hipSuccess) return RN_ERR_LAUNCH;
+    rn::ReduceArgs ra{static_cast<const float*>(workspace), dw, p.grid, (int)H};
+    if (rn::launch_bwd_reduce(ra, s) != hipSuccess) return RN_ERR_LAUNCH;
+    return RN_OK;
+}
+
 } // namespace
 
 // ===========================================================================
@@ -296,10 +440,10 @@ int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype, int 
     if (cu_count <= 0 || T < 0) return RN_ERR_SHAPE;
     Policy p{};
     int st;
-    if (op == 0 || op == 1) {
+    if (op == 0 || op == 1 || op == 3) {
         if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
         if ((st = check_h(H, x_dtype)) != RN_OK) return st;
-        st = op == 0 ? policy_fwd(T, H, x_dtype, cu_count, &p) : policy_bwd(T, H, x_dtype, cu_count, &p);
+        st = op == 1 ? policy_bwd(T, H, x_dtype, cu_count, &p) : policy_fwd(T, H, x_dtype, cu_count, &p, op == 3);
     } else if (op == 2) {
         if (x_dtype != RN_BF16 || w_dtype != RN_BF16) return RN_ERR_DTYPE;
         if (H <= 0 || H > RN_MAX_H || H % 128 != 0) return RN_ERR_SHAPE;
@@ -341,102 +485,31 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t H, int device)
 int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype, void* y, int64_t ldy,
                 float* rstd, int64_t T, int64_t H, float eps, void* stream)
 {
-    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
-    int st;
-    if ((st = check_h(H, x_dtype)) != RN_OK) return st;
-    if (T < 0) return RN_ERR_SHAPE;
-    Policy p{};
-    if ((st = policy_fwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
-    if (T == 0) return RN_OK;
-    if (!x || !w || !y || !rstd) return RN_ERR_NULL;
-    if ((st = check_matrix(x, ldx, H, x_dtype)) != RN_OK) return st;
-    if ((st = check_matrix(y, ldy, H, x_dtype)) != RN_OK) return st;
-    if (!aligned(w, 16) || !aligned(rstd, 4)) return RN_ERR_ALIGN;
-    const int xb = elem_bytes(x_dtype);
-    const Extent ex = mat_extent(x, T, H, ldx, xb), ey = mat_extent(y, T, H, ldy, xb);
-    const Extent ew = vec_extent(w, H, elem_bytes(w_dtype)), er = vec_extent(rstd, T, 4);
-    if (overlap(ey, ex) || overlap(ey, ew) || overlap(ey, er) || overlap(er, ex) || overlap(er, ew))
-        return RN_ERR_ALIAS;
+    return fwd_common(x, ldx, nullptr, 0, x_dtype, w, w_dtype, y, ldy, nullptr, 0, rstd, T, H, eps, stream, false);
+}
 
-    int cu = 0;
-    if ((st = current_device_cu(&cu)) != RN_OK) return st;
-    if ((st = policy_fwd(T, H, x_dtype, cu, &p)) != RN_OK) return st;
-    apply_override(0, T, (int)(H / elems_per_chunk(x_dtype)), &p);
-    log_policy("fwd", T, H, p);
-
-    rn::FwdArgs a{};
-    a.lpr = p.lpr; a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0; a.x = x; a.ldx = ldx; a.w = w; a.y = y; a.ldy = ldy; a.rstd = rstd;
-    a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype)); a.eps = eps;
-    clear_last_error();
-    if (rn::launch_fwd(a, x_dtype, w_dtype, p, (hipStream_t)stream) != hipSuccess) return RN_ERR_LAUNCH;
-    return RN_OK;
+int rmsnorm_fwd_residual(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dtype, const void* w,
+                         int w_dtype, void* y, int64_t ldy, void* h_out, int64_t ldh, float* rstd, int64_t T,
+                         int64_t H, float eps, void* stream)
+{
+    return fwd_common(x, ldx, u, ldu, x_dtype, w, w_dtype, y, ldy, h_out, ldh, rstd, T, H, eps, stream, true);
 }
 
 int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype,
                 const float* rstd, void* dx, int64_t lddx, float* dw, int64_t T, int64_t H, int deterministic,
                 void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
-    int st;
-    if ((st = check_h(H, x_dtype)) != RN_OK) return st;
-    if (T < 0) return RN_ERR_SHAPE;
-    Policy p{};
-    if ((st = policy_bwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
-    if (!dw) return RN_ERR_NULL;
-    if (!aligned(dw, 4)) return RN_ERR_ALIGN;
-    const int xb = elem_bytes(x_dtype);
-    const Extent edw = vec_extent(dw, H, 4);
-    Extent edy{}, ex{}, edx{}, ew{}, er{};
-    if (T > 0) {
-        if (!dy || !x || !w || !rstd || !dx) return RN_ERR_NULL;
-        if ((st = check_matrix(dy, lddy, H, x_dtype)) != RN_OK) return st;
-        if ((st = check_matrix(x, ldx, H, x_dtype)) != RN_OK) return st;
-        if ((st = check_matrix(dx, lddx, H, x_dtype)) != RN_OK) return st;
-        if (!aligned(w, 16) || !aligned(rstd, 4)) return RN_ERR_ALIGN;
-        edy = mat_extent(dy, T, H, lddy, xb);
-        ex = mat_extent(x, T, H, ldx, xb);
-        edx = mat_extent(dx, T, H, lddx, xb);
-        ew = vec_extent(w, H, elem_bytes(w_dtype));
-        er = vec_extent(rstd, T, 4);
-        if (overlap(edx, edy) || overlap(edx, ex) || overlap(edx, ew) || overlap(edx, er) || overlap(edx, edw) ||
-            overlap(edw, edy) || overlap(edw, ex) || overlap(edw, ew) || overlap(edw, er))
-            return RN_ERR_ALIAS;
-        if (!workspace) return RN_ERR_WORKSPACE;
-        if (!aligned(workspace, 16)) return RN_ERR_ALIGN;
-    }
+    return bwd_common(dy, lddy, x, ldx, x_dtype, w, w_dtype, rstd, nullptr, 0, dx, lddx, dw, T, H, deterministic,
+                      workspace, workspace_bytes, stream, false);
+}
 
-    int cu = 0;
-    if ((st = current_device_cu(&cu)) != RN_OK) return st;
-    clear_last_error();
-    hipStream_t s = (hipStream_t)stream;
-    if (T == 0) {
-        // No rows: the weight gradient is the empty sum.
-        if (rn::launch_fill_zero(dw, H, s) != hipSuccess) return RN_ERR_LAUNCH;
-        return RN_OK;
-    }
-    if ((st = policy_bwd(T, H, x_dtype, cu, &p)) != RN_OK) return st;
-    const size_t need = workspace_need(p.grid, H);
-    if (workspace_bytes < need) return RN_ERR_WORKSPACE;
-    {
-        const Extent ews = vec_extent(workspace, (int64_t)(need / 4), 4);
-        if (overlap(ews, edy) || overlap(ews, ex) || overlap(ews, ew) || overlap(ews, er) || overlap(ews, edx) ||
-            overlap(ews, edw))
-            return RN_ERR_ALIAS;
-    }
-    apply_override(1, T, (int)(H / elems_per_chunk(x_dtype)), &p);
-    log_policy("bwd", T, H, p);
-
-    rn::BwdArgs a{};
-    a.lpr = p.lpr; a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0; a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.w = w; a.rstd = rstd;
-    a.dx = dx; a.lddx = lddx; a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype));
-    a.inv_h = 1.0f / (float)H;
-    // Both modes run the same fixed-order reduction (see the header).
-    (void)deterministic;
-    a.part = static_cast<float*>(workspace);
-    if (rn::launch_bwd(a, x_dtype, w_dtype, p, s) != hipSuccess) return RN_ERR_LAUNCH;
-    rn::ReduceArgs ra{static_cast<const float*>(workspace), dw, p.grid, (int)H};
-    if (rn::launch_bwd_reduce(ra, s) != hipSuccess) return RN_ERR_LAUNCH;
-    return RN_OK;
+int rmsnorm_bwd_residual(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w,
+                         int w_dtype, const float* rstd, const void* g_residual, int64_t ldgr, void* dx,
+                         int64_t lddx, float* dw, int64_t T, int64_t H, int deterministic, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    return bwd_common(dy, lddy, x, ldx, x_dtype, w, w_dtype, rstd, g_residual, ldgr, dx, lddx, dw, T, H,
+                      deterministic, workspace, workspace_bytes, stream, true);
 }
 
 int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx, void* residual, int64_t ldr, const void* w,

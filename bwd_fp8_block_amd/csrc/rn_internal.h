@@ -23,9 +23,11 @@ constexpr int RN_FLAG_NT = 1;    // non-temporal (streaming) loads and stores
 constexpr int RN_FLAG_ILV = 2;   // interleaved row order (see RowWalk)
 
 struct FwdArgs {
-    int lpr;
-    int interleave;              // RN_FLAG_ILV set in the policy                     // lanes per row group (runtime for class 64)
+    int lpr;                     // lanes per row group (runtime for class 64)
+    int interleave;              // RN_FLAG_ILV set in the policy
     const void* x; int64_t ldx;
+    const void* u; int64_t ldu;  // residual form: the residual input
+    void* h; int64_t ldh;        // residual form: h_new = x + u, rounded to x's dtype
     const void* w;
     void* y; int64_t ldy;
     float* rstd;
@@ -40,6 +42,7 @@ struct BwdArgs {
     const void* x; int64_t ldx;
     const void* w;
     const float* rstd;
+    const void* gres; int64_t ldgr;   // residual form: gradient along the residual stream
     void* dx; int64_t lddx;
     float* part;                 // workspace: one fp32 dw partial per (row strip, column)
     int64_t T; int H; int nch;
@@ -69,8 +72,10 @@ struct Fp8Args {
 };
 
 // Launchers return hipSuccess or the launch error.  They assume validated args.
-hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s);
+// residual != 0 selects the training-pair variants that also read u (forward)
+// or g_residual (backward).
+hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_fp8(const Fp8Args& a, const Policy& p, hipStream_t s);

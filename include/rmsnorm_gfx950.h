@@ -1,11 +1,13 @@
 /*
  * rmsnorm_gfx950.h -- C ABI of the MI355X (gfx950) RMSNorm library.
  *
- * Three operations, each one or two HIP kernels enqueued on the caller's stream:
+ * Operations, each one or two HIP kernels enqueued on the caller's stream:
  *   rmsnorm_fwd                   y = x * rstd * w, plus the fp32 rstd per row
  *   rmsnorm_bwd                   dx and the fp32 weight gradient dw in one pass
- *                                 over the rows (deterministic or atomic dw)
+ *                                 over the rows (fixed-order, repeatable dw)
  *   add_rmsnorm_fp8_block_quant   residual add + RMSNorm + e4m3 1x128 block quant
+ *   rmsnorm_fwd_residual          training forward with a residual stream
+ *   rmsnorm_bwd_residual          its backward (adds the residual-stream gradient)
  *
  * Conventions shared by every entry point
  *   - Every function is extern "C", never throws, never allocates device or
@@ -25,10 +27,10 @@
  *     its 16-bit pattern).  (x, w) pairs accepted: (f32, f32), (bf16, bf16),
  *     (bf16, f32).  dy and dx always share x's dtype; rstd and dw are fp32.
  *   - T >= 0; T == 0 returns RN_OK and enqueues nothing (except that
- *     rmsnorm_bwd then sets dw to zero, the empty sum).  H >= 1, a multiple
+ *     the backwards then set dw to zero, the empty sum).  H >= 1, a multiple
  *     of 8 for bf16 rows and of 4 for f32 rows, and at most
- *       rmsnorm_fwd                  32768 (bf16 rows), 16384 (f32 rows)
- *       rmsnorm_bwd                  16384 (bf16 rows),  8192 (f32 rows)
+ *       rmsnorm_fwd[_residual]       32768 (bf16 rows), 16384 (f32 rows)
+ *       rmsnorm_bwd[_residual]       16384 (bf16 rows),  8192 (f32 rows)
  *       add_rmsnorm_fp8_block_quant  32768, a multiple of 128
  *     (RN_ERR_SHAPE beyond).
  *   - On any error the function returns a non-zero rn_status, enqueues
@@ -140,6 +142,50 @@ int rmsnorm_bwd(const void* dy, int64_t lddy,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training forward with a residual stream  ([C] API and Design: Forward: the
+ * forward that takes a residual returns h_new and normalises it).
+ *   h[r,j]  = round_dtype( x[r,j] + u[r,j] )             written to h_out
+ *   rstd[r] = 1 / sqrt( (sum_j h[r,j]^2) / H + eps )      (fp32)
+ *   y[r,j]  = round_dtype( h[r,j] * rstd[r] * w[j] )
+ * The sum is an fp32 addition rounded once to x's dtype (for two bf16 or two
+ * fp32 inputs that is the correctly rounded sum); the rest is as in
+ * rmsnorm_fwd, applied to h.  Same dtype pairs, limits and errors.
+ *   x      [T, ldx]  x_dtype   input
+ *   u      [T, ldu]  x_dtype   input (the residual stream)
+ *   w      [H]       w_dtype   input
+ *   y      [T, ldy]  x_dtype   output
+ *   h_out  [T, ldh]  x_dtype   output; may be exactly x or exactly u (same
+ *                              pointer and row stride: the update is then in
+ *                              place), otherwise it may not overlap them
+ *   rstd   [T]       fp32      output (what rmsnorm_bwd_residual expects)
+ */
+int rmsnorm_fwd_residual(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dtype,
+                         const void* w, int w_dtype,
+                         void* y, int64_t ldy, void* h_out, int64_t ldh, float* rstd,
+                         int64_t T, int64_t H, float eps, void* stream);
+
+/*
+ * Training backward with a residual stream  ([C] API and Design: Backward:
+ * the residual variant adds the gradient of the residual stream into the dx
+ * it returns, so both inputs of the add receive the same gradient).
+ * rmsnorm_bwd at x = the forward's h_out, plus
+ *   dx[r,j] = round_dtype( rstd[r]*(dy[r,j]*w[j] - c[r]*xhat[r,j]) + g_residual[r,j] )
+ * with the addition in fp32 before the one rounding.  dw does not depend on
+ * g_residual.  Same workspace, limits and errors as rmsnorm_bwd.
+ *   g_residual [T, ldgr] x_dtype  input; may be exactly dx (same pointer and
+ *                                 row stride: dx then accumulates in place),
+ *                                 otherwise it may not overlap dx
+ */
+int rmsnorm_bwd_residual(const void* dy, int64_t lddy,
+                         const void* x, int64_t ldx, int x_dtype,
+                         const void* w, int w_dtype,
+                         const float* rstd,
+                         const void* g_residual, int64_t ldgr,
+                         void* dx, int64_t lddx, float* dw,
+                         int64_t T, int64_t H, int deterministic,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fused residual add + RMSNorm + FP8 e4m3 1x128 block quant
  * ([F] description: Kernel and API; review thread on the scale layout).
  * bf16 only; H a multiple of 128.  Per row r:
@@ -175,7 +221,8 @@ int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx,
 
 /*
  * Host-only launch policy query (no HIP call; usable without a GPU).
- * op: 0 = forward, 1 = backward, 2 = fused fp8 producer.
+ * op: 0 = forward, 1 = backward (plain and residual form), 2 = fused fp8
+ * producer, 3 = forward with a residual stream.
  * Fills out[0..6] = { lanes per row, 16-byte vectors per lane, threads per
  * work-group, work-groups (row chunks), rows per work-group pass, kernel id,
  * flags (bit 0: non-temporal streaming loads/stores) }

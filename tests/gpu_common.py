@@ -82,3 +82,36 @@ def sample_rows(T: int, n: int = 48, seed: int = 0):
     rows = {0, T - 1, T // 2, max(T - 2, 0), min(1, T - 1)}
     rows.update(rng.choice(T, size=min(n, T), replace=False).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+SENTINEL_BF16 = 0x7FBF      # a NaN pattern no kernel writes
+
+
+def guarded_matrix(T, H, dtype, ld=None, guard=64):
+    """A [T, ld] buffer plus guard elements on both sides, filled with a sentinel.
+    Returns (full flat tensor, [T, H] view with row stride ld)."""
+    ld = ld or H
+    n = guard + T * ld + guard
+    if dtype == torch.bfloat16:
+        full = torch.full((n,), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    elif dtype == torch.uint8:
+        full = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    else:
+        full = torch.full((n,), float("nan"), dtype=dtype, device="cuda")
+    view = full[guard: guard + T * ld].view(T, ld)[:, :H] if T > 0 else full[guard:guard].view(0, H)
+    return full, view
+
+
+def assert_guards(full: torch.Tensor, T, H, ld, guard=64, name="out"):
+    """The guard bands (and the row padding beyond column H) still hold the sentinel."""
+    h = to_host(full)
+    if full.dtype == torch.bfloat16:
+        sent = lambda a: a == SENTINEL_BF16
+    elif full.dtype == torch.uint8:
+        sent = lambda a: a == 0xA5
+    else:
+        sent = lambda a: np.isnan(a)
+    assert sent(h[:guard]).all() and sent(h[guard + T * ld:]).all(), "%s: guard band overwritten" % name
+    if ld > H and T > 0:
+        body = h[guard: guard + T * ld].reshape(T, ld)
+        assert sent(body[:, H:]).all(), "%s: row padding overwritten" % name

@@ -9,14 +9,11 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import (as_f64, check_dw, check_rstd, check_values, sample_rows, to_dev, to_host,
-                        torch_dtype)
+from gpu_common import (as_f64, assert_guards, check_dw, check_rstd, check_values, guarded_matrix, sample_rows,
+                        to_dev, to_host, torch_dtype)
 from workloads import CONFIGS, Workload, generate
 
 pytestmark = pytest.mark.gpu
-
-SENTINEL_BF16 = 0x7FBF      # a NaN pattern no kernel writes
-SENTINEL_F32 = np.float32(np.nan)
 
 
 @pytest.fixture(scope="module")
@@ -24,35 +21,6 @@ def rn():
     import bwd_fp8_block_amd as m
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     return m
-
-
-def guarded_matrix(T, H, dtype, ld=None, guard=64):
-    """A [T, ld] buffer plus guard elements on both sides, filled with a sentinel.
-    Returns (full flat tensor, [T, H] view with row stride ld)."""
-    ld = ld or H
-    n = guard + T * ld + guard
-    if dtype == torch.bfloat16:
-        full = torch.full((n,), SENTINEL_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    elif dtype == torch.uint8:
-        full = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
-    else:
-        full = torch.full((n,), float("nan"), dtype=dtype, device="cuda")
-    view = full[guard: guard + T * ld].view(T, ld)[:, :H] if T > 0 else full[guard:guard].view(0, H)
-    return full, view
-
-
-def assert_guards(full: torch.Tensor, T, H, ld, guard=64, name="out"):
-    h = to_host(full)
-    if full.dtype == torch.bfloat16:
-        sent = lambda a: a == SENTINEL_BF16
-    elif full.dtype == torch.uint8:
-        sent = lambda a: a == 0xA5
-    else:
-        sent = lambda a: np.isnan(a)
-    assert sent(h[:guard]).all() and sent(h[guard + T * ld:]).all(), "%s: guard band overwritten" % name
-    if ld > H and T > 0:
-        body = h[guard: guard + T * ld].reshape(T, ld)
-        assert sent(body[:, H:]).all(), "%s: row padding overwritten" % name
 
 
 def gpu_fwd(rn, x: np.ndarray, w: np.ndarray, eps: float, ld_pad=0):

@@ -47,13 +47,14 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_scale: float = 50.0
     residual: bool = False
+    g_residual: bool = False
     seed: int = SEED_BASE
 
 
 def generate(wl: Workload):
-    """Draw x, w, dy (and residual) for a workload.
+    """Draw x, w, dy (and residual, g_residual) for a workload.
 
-    Draw order is x, w, dy, residual from one PCG64 stream seeded with
+    Draw order is x, w, dy, residual, g_residual from one PCG64 stream seeded with
     ``wl.seed``.  Outlier rows (a fraction ``outlier_frac`` of T, chosen by a
     seeded permutation) are multiplied by ``outlier_scale`` in fp32 before the
     cast to the storage dtype."""
@@ -65,13 +66,16 @@ def generate(wl: Workload):
     w = (1.0 + 0.1 * rng.standard_normal((H,), dtype=np.float32)).astype(np.float32)
     dy = rng.standard_normal((T, H), dtype=np.float32)
     res = rng.standard_normal((T, H), dtype=np.float32) if wl.residual else None
+    gres = rng.standard_normal((T, H), dtype=np.float32) if wl.g_residual else None
     if wl.outlier_frac > 0.0 and T > 0:
         n_out = int(round(wl.outlier_frac * T))
         perm = np.random.Generator(np.random.PCG64(wl.seed + 1)).permutation(T)[:n_out]
         x[np.sort(perm)] *= np.float32(wl.outlier_scale)
     out = dict(x=_cast(x, wl.x_dtype), w=_cast(w, wl.w_dtype), dy=_cast(dy, wl.x_dtype))
     if res is not None:
-        out["residual"] = _cast(res, "bf16")
+        out["residual"] = _cast(res, wl.x_dtype)
+    if gres is not None:
+        out["g_residual"] = _cast(gres, wl.x_dtype)
     return out
 
 
@@ -87,4 +91,7 @@ CONFIGS = {
     "bf16_T65536_H5120_f32w": Workload("bf16_T65536_H5120_f32w", 65536, 5120, "bf16", "f32", seed=SEED_BASE + 500),
     "fp8_T8192_H4096": Workload("fp8_T8192_H4096", 8192, 4096, "bf16", "bf16", residual=True,
                                 seed=SEED_BASE + 600),
+    # the training pair with a residual stream (x, u, dy, g_residual all standard normal)
+    "res_bf16_T8192_H4096": Workload("res_bf16_T8192_H4096", 8192, 4096, "bf16", "bf16", residual=True,
+                                     g_residual=True, seed=SEED_BASE + 700),
 }
