@@ -9,13 +9,19 @@ Each op reads its own buffers, and two buffer sets alternate between steps
 (1.3 GB in flight), so no op finds its inputs in the 256 MB Infinity Cache
 left by the op before it; inputs are resident in HBM when timing starts.
 
+After the timed steps, the training pair with a residual stream is timed the
+same way at the same shape and reported under "next_ops" (not part of value):
+    rmsnorm_fwd_residual   (x, u -> y, h_new, rstd)      4*T*H*2 + 2*H + 4*T
+    rmsnorm_bwd_residual   (dy, h_new, rstd, g_residual -> dx, dw)
+                                                          4*T*H*2 + 2*H + 4*T + 4*H
+
 value = algorithmic bytes of a step / wall time per step (GB/s).  Algorithmic
 bytes count each tensor once (weight once, not per row):
     fwd  2*T*H*2 + 2*H + 4*T
     bwd  3*T*H*2 + 2*H + 4*T + 4*H
     fp8  9*T*H + 2*H + 4*(H/128)*round_up(T,4)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next]
 """
 import argparse
 import hashlib
@@ -36,7 +42,9 @@ KERNEL_SOURCES = {
     "bwd": ["bwd_fp8_block_amd/csrc/rn_bwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
     "fp8": ["bwd_fp8_block_amd/csrc/rn_fp8.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
 }
-KERNEL_NAMES = {"fwd": "k_rmsnorm_fwd", "bwd": "k_rmsnorm_bwd + k_dw_reduce", "fp8": "k_add_rmsnorm_fp8"}
+KERNEL_NAMES = {"fwd": "k_rmsnorm_fwd", "bwd": "k_rmsnorm_bwd + k_dw_reduce", "fp8": "k_add_rmsnorm_fp8",
+                "fwd_residual": "k_rmsnorm_fwd (residual form)",
+                "bwd_residual": "k_rmsnorm_bwd (residual form) + k_dw_reduce"}
 
 
 def algorithmic_bytes(T, H):
@@ -45,6 +53,13 @@ def algorithmic_bytes(T, H):
         "fwd": 2 * T * H * 2 + 2 * H + 4 * T,
         "bwd": 3 * T * H * 2 + 2 * H + 4 * T + 4 * H,
         "fp8": 9 * T * H + 2 * H + 4 * (H // 128) * ru4,
+    }
+
+
+def next_bytes(T, H):
+    return {
+        "fwd_residual": 4 * T * H * 2 + 2 * H + 4 * T,
+        "bwd_residual": 4 * T * H * 2 + 2 * H + 4 * T + 4 * H,
     }
 
 
@@ -96,6 +111,61 @@ def plan_step(rn, s):
             rn.plan_rmsnorm_bwd(s["dy2"], s["x2"], s["w"], s["r2"], s["dx2"], s["dw2"], deterministic=True,
                                 workspace=s["ws2"]),
             rn.plan_add_rmsnorm_fp8_block_quant(s["x3"], s["res3"], s["w"], s["out3"], s["sc3"], s["n3"], EPS))
+
+
+def make_res_set(torch, gen, dev, T, H, rn):
+    """Buffers of the training pair with a residual stream."""
+    bf = torch.bfloat16
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(bf)
+
+    s = {"w": (1.0 + 0.1 * torch.randn(H, generator=gen, device=dev)).to(bf)}
+    s["x"], s["u"] = randn(T, H), randn(T, H)
+    s["y"], s["h"] = torch.empty(T, H, dtype=bf, device=dev), torch.empty(T, H, dtype=bf, device=dev)
+    s["r"] = torch.empty(T, dtype=torch.float32, device=dev)
+    s["dy"], s["gr"] = randn(T, H), randn(T, H)
+    s["hb"] = torch.empty(T, H, dtype=bf, device=dev)
+    s["rb"] = torch.empty(T, dtype=torch.float32, device=dev)
+    s["dx"] = torch.empty(T, H, dtype=bf, device=dev)
+    s["dw"] = torch.empty(H, dtype=torch.float32, device=dev)
+    s["ws"] = torch.empty(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4, dtype=torch.float32, device=dev)
+    # the backward's h_new and rstd come from a residual forward over its own inputs
+    tmp = torch.empty(T, H, dtype=bf, device=dev)
+    rn.rmsnorm_fwd_residual(randn(T, H), randn(T, H), s["w"], tmp, s["hb"], s["rb"], EPS)
+    del tmp
+    return s
+
+
+def time_next(torch, rn, gen, dev, T, H, K, W):
+    """Per-launch times of the residual training pair (two alternating buffer sets)."""
+    sets = [make_res_set(torch, gen, dev, T, H, rn) for _ in range(2)]
+    plans = [(rn.plan_rmsnorm_fwd_residual(s["x"], s["u"], s["w"], s["y"], s["h"], s["r"], EPS),
+              rn.plan_rmsnorm_bwd_residual(s["dy"], s["hb"], s["w"], s["rb"], s["gr"], s["dx"], s["dw"],
+                                           deterministic=True, workspace=s["ws"])) for s in sets]
+    for i in range(W):
+        for f in plans[i % 2]:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        fwd, bwd = plans[i % 2]
+        evs[i][0].record()
+        fwd()
+        evs[i][1].record()
+        bwd()
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    per = {"fwd_residual": sum(e[0].elapsed_time(e[1]) for e in evs) / K,
+           "bwd_residual": sum(e[1].elapsed_time(e[2]) for e in evs) / K}
+    b = next_bytes(T, H)
+    out = {}
+    for k, ms in per.items():
+        gbs = b[k] / (ms * 1e-3) / 1e9
+        out[k] = {"kernel": KERNEL_NAMES[k], "bytes": b[k], "us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                  "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    del sets, plans
+    return out
 
 
 def run_step(calls, ev=None):
@@ -159,6 +229,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the residual training pair timing")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
@@ -220,6 +291,11 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": counters_for(dom)}
 
+    next_ops = None
+    if not args.no_next:
+        del sets, plans
+        next_ops = time_next(torch, rn, gen, dev, T, H, K, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(T, H)
@@ -243,6 +319,7 @@ def main():
         "ops": ops,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "next_ops": next_ops,
     }
     print(json.dumps(out), flush=True)
 

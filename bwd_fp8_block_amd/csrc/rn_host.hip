@@ -98,14 +98,13 @@ int elem_bytes(int dt) { return dt == RN_BF16 ? 2 : 4; }
 // Launch policies (pure functions of the shape and the CU count).
 // ---------------------------------------------------------------------------
 
-// Forward.  Measured on MI355X (T = 8192): rows split over two wavefronts
-// with at most 4-8 vectors of 16 bytes per lane, walked as one interleaved
-// window, run at 0.95-0.97 of a same-traffic streaming copy for H = 2048 ..
-// 5120.  Short rows use 16/32/64-lane groups; very long rows more wavefronts.
-// The residual form holds two input rows per buffer: at four vectors per lane
-// three 256-thread work-groups fit on a CU (one beyond eight vectors), and the
-// grid is one full wave of them.
-int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p, bool residual = false)
+// Forward.  Rows split over two wavefronts with at most 4-8 vectors of 16
+// bytes per lane, walked as one interleaved window.  Short rows use 16/32/64
+// lane groups; very long rows more wavefronts.  Work-groups per CU, measured
+// on MI355X (H = 2048 .. 5120): four while T is at most 48 rows per CU (T =
+// 8192: 0.95-0.97 of a same-traffic streaming copy), two beyond (T = 16384 ..
+// 65536: 0.94-0.97, where four fall to 0.87-0.94).
+int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int nch = (int)(H / elems_per_chunk(x_dtype));
     if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
@@ -118,12 +117,30 @@ int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p, bool residu
     if (p->lpr > 512) return RN_ERR_SHAPE;
     p->wgs = wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
-    const int64_t per_cu = p->nv <= 2 ? 4 : p->nv <= 4 ? (residual ? 3 : 4) : (residual ? 1 : 2);
+    const int64_t per_cu = p->nv <= 4 ? (T <= 48 * (int64_t)cu ? 4 : 2) : 2;
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
     p->kernel = 0;
     p->flags = RN_FLAG_NT_DEFAULT | rn::RN_FLAG_ILV;
+    return RN_OK;
+}
+
+// The residual form reads two rows (x, u) and writes two (y, h_new) for every
+// row of the plain forward: same row geometry, half the work-groups.
+// Measured on MI355X: two per CU up to 64 rows per CU (T = 8192, H = 2048 ..
+// 4096: 0.95-0.97 of a same-traffic copy), one beyond (T = 32768 .. 65536:
+// 0.91-0.95) and for rows of more than four vectors per lane (T = 8192,
+// H = 5120 / 7168: 0.89 / 0.93).
+int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
+{
+    const int st = policy_fwd(T, H, x_dtype, cu, p);
+    if (st != RN_OK) return st;
+    const int64_t per_cu = (p->nv <= 4 && T <= 64 * (int64_t)cu) ? 2 : 1;
+    int64_t g = ceil_div(T, p->gpw);
+    if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
+    p->grid = g < 1 ? 1 : g;
+    p->kernel = 3;
     return RN_OK;
 }
 
@@ -280,7 +297,10 @@ int fwd_common(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dty
     if ((st = check_h(H, x_dtype)) != RN_OK) return st;
     if (T < 0) return RN_ERR_SHAPE;
     Policy p{};
-    if ((st = policy_fwd(T, H, x_dtype, 1, &p)) != RN_OK) return st;      // shape range (CU-independent)
+    auto policy = [&](int cu, Policy* q) {
+        return residual ? policy_fwd_residual(T, H, x_dtype, cu, q) : policy_fwd(T, H, x_dtype, cu, q);
+    };
+    if ((st = policy(1, &p)) != RN_OK) return st;                           // shape range (CU-independent)
     if (T == 0) return RN_OK;
     if (!x || !w || !y || !rstd) return RN_ERR_NULL;
     if (residual && (!u || !h)) return RN_ERR_NULL;
@@ -306,7 +326,7 @@ int fwd_common(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dty
 
     int cu = 0;
     if ((st = current_device_cu(&cu)) != RN_OK) return st;
-    if ((st = policy_fwd(T, H, x_dtype, cu, &p, residual)) != RN_OK) return st;
+    if ((st = policy(cu, &p)) != RN_OK) return st;
     apply_override(0, T, (int)(H / elems_per_chunk(x_dtype)), &p);
     log_policy(residual ? "fwd_residual" : "fwd", T, H, p);
 
@@ -443,7 +463,9 @@ int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype, int 
     if (op == 0 || op == 1 || op == 3) {
         if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
         if ((st = check_h(H, x_dtype)) != RN_OK) return st;
-        st = op == 1 ? policy_bwd(T, H, x_dtype, cu_count, &p) : policy_fwd(T, H, x_dtype, cu_count, &p, op == 3);
+        st = op == 1 ? policy_bwd(T, H, x_dtype, cu_count, &p)
+           : op == 3 ? policy_fwd_residual(T, H, x_dtype, cu_count, &p)
+                     : policy_fwd(T, H, x_dtype, cu_count, &p);
     } else if (op == 2) {
         if (x_dtype != RN_BF16 || w_dtype != RN_BF16) return RN_ERR_DTYPE;
         if (H <= 0 || H > RN_MAX_H || H % 128 != 0) return RN_ERR_SHAPE;

@@ -62,6 +62,9 @@ CU = 256
     (2, 4096, 7168, 1, 1), (2, 8192, 4096, 1, 1), (2, 3, 1152, 1, 1), (2, 1, 128, 1, 1),
     (0, 5, 8, 1, 1), (1, 5, 8, 1, 1), (0, 100, 32768, 1, 1), (1, 9, 16384, 1, 1), (2, 9, 32768, 1, 1),
     (0, 7, 17408, 1, 1), (2, 7, 17408, 1, 1), (0, 7, 9216, 0, 0), (2, 7, 9216, 1, 1), (0, 3, 20480, 1, 0),
+    (3, 8192, 4096, 1, 1), (3, 64, 256, 0, 0), (3, 5, 8, 1, 1), (3, 100, 120, 1, 1), (3, 33, 5120, 1, 0),
+    (3, 17, 7168, 1, 1), (3, 9, 8200, 1, 1), (3, 5, 16384, 1, 1), (3, 3, 16384, 0, 0), (3, 2, 32768, 1, 1),
+    (3, 1000, 128, 1, 1), (3, 300, 3072, 1, 1), (3, 7, 17408, 1, 1),
 ])
 def test_policy_invariants(rn, op, T, H, xd, wd):
     p = rn.rn_query_policy(op, T, H, xd, wd, CU)
@@ -76,7 +79,7 @@ def test_policy_invariants(rn, op, T, H, xd, wd):
         assert p["lpr"] % 16 == 0                            # 1x128 block = 16 lanes
     # a compiled variant serves it: the same check the library applies to overrides
     lprc = min(p["lpr"], 64)
-    if op in (0, 2):
+    if op in (0, 2, 3):
         assert (lprc, p["nv"]) in {(16, 1), (16, 2), (16, 4), (32, 1), (32, 2), (32, 4)} or \
             (lprc == 64 and (p["wgs"] <= 256 and 1 <= p["nv"] <= 8 or p["wgs"] <= 512 and 5 <= p["nv"] <= 8))
     else:
@@ -92,6 +95,10 @@ def test_policy_shapes_of_the_workloads(rn):
     assert b["nv"] == 1 and b["lpr"] == 512 and b["grid"] == 256
     q = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
     assert q["lpr"] == 256 and q["nv"] == 4 and q["grid"] == 512
+    r = rn.rn_query_policy(3, 8192, 4096, 1, 1, CU)
+    assert r["lpr"] == 128 and r["nv"] == 4 and r["grid"] == 512 and r["flags"] & 3 == 3
+    assert rn.rn_query_policy(0, 65536, 4096, 1, 1, CU)["grid"] == 512
+    assert rn.rn_query_policy(3, 65536, 4096, 1, 1, CU)["grid"] == 256
 
 
 def test_policy_rejects_out_of_range(rn):
