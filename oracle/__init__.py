@@ -70,6 +70,8 @@ def _load():
     lib.rno_rmsnorm_fwd_residual.restype = i32
     lib.rno_rmsnorm_bwd_residual.argtypes = [vp, i64, vp, i64, i32, vp, i32, vp, vp, i64, i64, i64, vp, i64, vp]
     lib.rno_rmsnorm_bwd_residual.restype = i32
+    lib.rno_rmsnorm_fwd_heads.argtypes = [vp, i64, i64, i32, vp, i32, i64, i64, i64, f32, vp, vp]
+    lib.rno_rmsnorm_fwd_heads.restype = i32
     _lib = lib
     return lib
 
@@ -239,3 +241,22 @@ def rmsnorm_bwd_residual(dy: np.ndarray, h: np.ndarray, w: np.ndarray, rstd: np.
     if rc:
         raise ValueError("oracle rmsnorm_bwd_residual rejected the arguments (%d)" % rc)
     return dx, dw
+
+
+def rmsnorm_fwd_heads(x: np.ndarray, heads: int, head_dim: int, w: np.ndarray, eps: float,
+                      ld_head: int | None = None, want_y: bool = True):
+    """Per-head RMSNorm over a [T, >= (heads-1)*ld_head + head_dim] array (float32 or uint16 bf16
+    bits, contiguous columns): row (t, h) is x[t, h*ld_head : h*ld_head + head_dim].
+    Returns (y [T, heads, head_dim] float64 unrounded or None, rstd [T, heads] float64)."""
+    lib = _load()
+    T = x.shape[0]
+    ld_head = head_dim if ld_head is None else ld_head
+    assert x.ndim == 2 and x.shape[1] >= (heads - 1) * ld_head + head_dim
+    y = np.empty((T, heads, head_dim), dtype=np.float64) if want_y else None
+    rstd = np.empty((T, heads), dtype=np.float64)
+    rc = lib.rno_rmsnorm_fwd_heads(_ptr(x), _row_stride(x) if T else x.shape[1], ld_head, _dtype_code(x),
+                                   _ptr(w), _dtype_code(w), T, heads, head_dim, np.float32(eps),
+                                   _ptr(y), _ptr(rstd))
+    if rc:
+        raise ValueError("oracle rmsnorm_fwd_heads rejected the arguments (%d)" % rc)
+    return y, rstd

@@ -27,6 +27,9 @@
  *    pre-norm sum, bf16 normed output, fp32 scale = amax/448 per 1x128 block
  *    in the column-major (H/128, round_up(T,4)) layout, e4m3 codes quantised
  *    from the bf16-rounded normed values.
+ *  - FlashInfer PR #6332 (QKV projection + QK-RMSNorm + RoPE overlapped with
+ *    the Ulysses head exchange), Description, operator math: per-head fp32
+ *    RMSNorm over head_dim with one shared weight per Q or K.
  *
  * Readings taken where the pages are silent (each is also listed in the
  * design notes of the repository):
@@ -48,6 +51,9 @@
  *  R12 the training backward with a residual-stream gradient returns
  *      dx_total = dx + g_residual, the sum taken before the one rounding
  *      into the output dtype; dw is unchanged by g_residual.
+ *  R13 per-head RMSNorm treats every (token, head) slice of head_dim
+ *      contiguous values as one row, with the same [head_dim] weight for all
+ *      heads; rstd is indexed token-major, rstd[t*heads + h].
  */
 #include <math.h>
 #include <stddef.h>
@@ -407,5 +413,34 @@ int rno_rmsnorm_bwd_residual(const void* dy, int64_t lddy,
         for (int64_t r = 0; r < T; ++r)
             for (int64_t j = 0; j < H; ++j)
                 dx[r * lddx + j] += load_elem(g_res, x_dtype, r * ldgr + j);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-head RMSNorm (QK-norm).                                               */
+/* FlashInfer PR #6332 (QKV projection + QK-RMSNorm + RoPE overlapped with  */
+/* the Ulysses head exchange), Description, operator math: an fp32 RMSNorm with */
+/* eps 1e-6 over each head's head_dim values, one shared [head_dim] weight   */
+/* per Q or K.  Row (t, h) starts at element t*ld_token + h*ld_head of x.    */
+/* y is returned unrounded and dense, y[(t*heads + h)*D + j] (reading R13).  */
+/* ------------------------------------------------------------------------ */
+
+int rno_rmsnorm_fwd_heads(const void* x, int64_t ld_token, int64_t ld_head, int x_dtype,
+                          const void* w, int w_dtype,
+                          int64_t T, int64_t heads, int64_t D, float eps,
+                          double* y,                   /* may be NULL; [T*heads, D] */
+                          double* rstd)                /* may be NULL; [T*heads] */
+{
+    if (T < 0 || heads <= 0 || D <= 0) return 1;
+    size_t es = x_dtype == RNO_BF16 ? 2 : 4;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < heads; ++h) {
+            int64_t r = t * heads + h;
+            const char* row = (const char*)x + (size_t)(t * ld_token + h * ld_head) * es;
+            int rc = rno_rmsnorm_fwd(row, D, x_dtype, w, w_dtype, 1, D, eps,
+                                     y ? y + r * D : NULL, D, rstd ? rstd + r : NULL);
+            if (rc) return rc;
+        }
+    }
     return 0;
 }
