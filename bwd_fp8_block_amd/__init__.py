@@ -25,11 +25,13 @@ __all__ = [
     "rn_selftest_quant", "rn_selftest_cvt_e4m3",
     "plan_rmsnorm_fwd", "plan_rmsnorm_bwd", "plan_add_rmsnorm_fp8_block_quant",
     "rmsnorm_fwd_residual", "rmsnorm_bwd_residual", "plan_rmsnorm_fwd_residual", "plan_rmsnorm_bwd_residual",
+    "rmsnorm_fwd_heads", "plan_rmsnorm_fwd_heads", "RN_HEADS_MAX_VECTORS",
 ]
 
 RN_F32 = 0
 RN_BF16 = 1
 RN_MAX_H = 32768
+RN_HEADS_MAX_VECTORS = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "librmsnorm_gfx950.so")
@@ -63,6 +65,9 @@ lib.rmsnorm_fwd_residual.restype = _i32
 lib.rmsnorm_bwd_residual.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp,
                                      _i64, _i64, _i32, _vp, _sz, _vp]
 lib.rmsnorm_bwd_residual.restype = _i32
+lib.rmsnorm_fwd_heads.argtypes = [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
+                                  _f32, _vp]
+lib.rmsnorm_fwd_heads.restype = _i32
 lib.rn_query_policy.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.rn_query_policy.restype = _i32
 lib.rn_bwd_workspace_bytes_for.argtypes = [_i64, _i64, _i32]
@@ -305,6 +310,48 @@ def rmsnorm_bwd_residual(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rst
     _check("rmsnorm_bwd_residual", st)
 
 
+def _heads(t: torch.Tensor, name: str):
+    """(pointer, token stride, head stride) of a [T, heads, head_dim] view with contiguous head_dim."""
+    if t.dim() != 3:
+        raise ValueError("%s must be 3-D [T, heads, head_dim]" % name)
+    T, nh, D = t.shape
+    if T > 0 and D > 1 and t.stride(2) != 1:
+        raise ValueError("%s must have a contiguous head_dim" % name)
+    ld_h = t.stride(1) if nh > 1 else D
+    ld_t = t.stride(0) if T > 1 else (nh - 1) * ld_h + D
+    return t.data_ptr(), ld_t, ld_h
+
+
+def _prep_fwd_heads(x, w, y, rstd, eps):
+    dev = _dev((x, w, y, rstd))
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("rmsnorm_fwd_heads: y must match x in shape and dtype")
+    T, nh, D = x.shape
+    if w.shape != (D,):
+        raise ValueError("rmsnorm_fwd_heads: w must be [head_dim]")
+    pr = None
+    if rstd is not None:
+        if rstd.dtype != torch.float32 or rstd.numel() != T * nh or not rstd.is_contiguous():
+            raise ValueError("rmsnorm_fwd_heads: rstd must be contiguous float32 with T*heads elements")
+        pr = rstd.data_ptr()
+    px, ldt, ldh = _heads(x, "x")
+    py, ldyt, ldyh = _heads(y, "y")
+    with _on(dev):
+        args = (px, ldt, ldh, _dt(x), _vec(w, "w"), _dt(w), py, ldyt, ldyh, pr, T, nh, D, float(eps), _stream(dev))
+    return dev, lib.rmsnorm_fwd_heads, args
+
+
+def rmsnorm_fwd_heads(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: torch.Tensor | None,
+                      eps: float) -> None:
+    """Per-head RMSNorm over x viewed as [T, heads, head_dim] (any token and head strides, contiguous
+    head_dim), shared weight w [head_dim]; y has the same shape and may be x itself (in place).
+    rstd: float32 with T*heads elements (token-major) or None."""
+    dev, fn, args = _prep_fwd_heads(x, w, y, rstd, eps)
+    with _on(dev):
+        st = fn(*args)
+    _check("rmsnorm_fwd_heads", st)
+
+
 def _plan(name, prep):
     dev, fn, args = prep
     cur = torch.cuda.current_device
@@ -343,6 +390,11 @@ def plan_rmsnorm_bwd_residual(dy, x, w, rstd, g_residual, dx, dw, deterministic=
     """Planned rmsnorm_bwd_residual (see plan_rmsnorm_fwd)."""
     return _plan("rmsnorm_bwd_residual",
                  _prep_bwd_residual(dy, x, w, rstd, g_residual, dx, dw, deterministic, workspace))
+
+
+def plan_rmsnorm_fwd_heads(x, w, y, rstd, eps):
+    """Planned rmsnorm_fwd_heads (see plan_rmsnorm_fwd)."""
+    return _plan("rmsnorm_fwd_heads", _prep_fwd_heads(x, w, y, rstd, eps))
 
 
 def rn_query_policy(op: int, T: int, H: int, x_dtype: int, w_dtype: int, cu_count: int) -> dict:

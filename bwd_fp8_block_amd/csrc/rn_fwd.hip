@@ -17,17 +17,27 @@
 // clamped in-bounds address and are zeroed, which keeps the loads in one
 // unbranched batch.  NT selects non-temporal (streaming) loads and stores.
 //
-// Residual form (RES; [C] API and Design: Forward, the training forward with
-// a residual): the row read is h_new = x + u, added in fp32 and rounded once
-// to x's dtype, stored, and normalised in place of x.
+// Forms (MODE):
+//   FWD_PLAIN     rows r = 0 .. T-1 at x + r*ldx.
+//   FWD_RESIDUAL  ([C] API and Design: Forward, the training forward with a
+//                 residual): the row read is h_new = x + u, added in fp32 and
+//                 rounded once to x's dtype, stored, and normalised in place
+//                 of x.
+//   FWD_HEADS     per-head RMSNorm ([Q] = FlashInfer PR #6332, QKV projection
+//                 + QK-RMSNorm + RoPE overlapped with the Ulysses head exchange,
+//                 Description, operator math): row r = t*heads + h is the
+//                 head_dim slice at x + t*ldx + h*ldxh, with the shared
+//                 head_dim weight; rstd[r] is optional.
 #include "rn_device.h"
 #include "rn_internal.h"
 
 namespace rn {
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, bool RES>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, int MODE>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 {
+    constexpr bool RES = MODE == FWD_RESIDUAL;
+    constexpr bool HEADS = MODE == FWD_HEADS;
     constexpr int E = Elems<XT>::value;
     constexpr int WPER = (WT == DT_F32) ? 4 : 8;    // w values per 16-byte word
     constexpr int WCH = E / WPER;                   // w words per x chunk
@@ -72,13 +82,31 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     // address is clamped to the chunk's last row (nothing is stored for it).
     // Loaded registers are not touched until they are used, so the loads of
     // the next row stay in flight while the current row is processed.
+    // Element offsets of row r in x and in y (and h_new, u).
+    auto xoff = [&](int64_t r) -> int64_t {
+        if constexpr (HEADS) {
+            const uint32_t rr = (uint32_t)r, t = rr / (uint32_t)a.heads;   // rows < 2^31 (host check)
+            return (int64_t)t * a.ldx + (int64_t)(rr - t * (uint32_t)a.heads) * a.ldxh;
+        } else {
+            return r * a.ldx;
+        }
+    };
+    auto yoff = [&](int64_t r) -> int64_t {
+        if constexpr (HEADS) {
+            const uint32_t rr = (uint32_t)r, t = rr / (uint32_t)a.heads;
+            return (int64_t)t * a.ldy + (int64_t)(rr - t * (uint32_t)a.heads) * a.ldyh;
+        } else {
+            return r * a.ldy;
+        }
+    };
+
     struct RowBuf {
         u32x4 v[NV];
         u32x4 u[RES ? NV : 1];
     };
     auto load = [&](RowBuf& b, int it) {
         const int64_t rr = W.clamp(W.row(it));
-        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * XB);
+        const u32x4* row = reinterpret_cast<const u32x4*>(xbase + xoff(rr) * XB);
 #pragma unroll
         for (int i = 0; i < NV; ++i) b.v[i] = ld16<NT>(row + cix[i]);
         if constexpr (RES) {
@@ -118,7 +146,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
         const float ms = ss / (float)a.H;
         const float rs = 1.0f / __builtin_sqrtf(ms + a.eps);
         if (valid) {
-            u32x4* yrow = reinterpret_cast<u32x4*>(ybase + r * a.ldy * XB);
+            u32x4* yrow = reinterpret_cast<u32x4*>(ybase + yoff(r) * XB);
             if constexpr (RES) {
                 u32x4* hrow = reinterpret_cast<u32x4*>(hbase + r * a.ldh * XB);
 #pragma unroll
@@ -140,7 +168,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
                 for (int e = 0; e < E; ++e) o[e] = (f[e] * rs) * wf[e];
                 if (cok[i]) st16<NT>(yrow + cix[i], pack<XT>(o));
             }
-            if (lane == 0) a.rstd[r] = rs;
+            if (lane == 0 && (!HEADS || a.rstd)) a.rstd[r] = rs;
         }
     };
 
@@ -153,23 +181,35 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 // Variant table and dispatch: template on the group class (16, 32, 64+) and
 // on the vectors per lane; the group width for class 64 is a launch argument.
 // ---------------------------------------------------------------------------
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool RES>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, int MODE>
 static hipError_t fwd_go(const FwdArgs& a, const Policy& p, hipStream_t s)
 {
     const dim3 g((unsigned)p.grid), b(p.wgs);
-    // The residual form is compiled with streaming accesses only.
-    const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
-    if constexpr (NV <= 4) {
-        // short per-lane rows: a third row buffer is affordable
-        if (((p.flags >> 4) & 7) == 3) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 3, RES>), g, b, 0, s, a);
-            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 3, false>), g, b, 0, s, a);
+    if constexpr (MODE == FWD_HEADS) {
+        // per-head rows are short (head_dim <= 128 vectors): sub-wave groups,
+        // streaming accesses, two row buffers
+        if constexpr (LPRC < 64 && NV <= 4) {
+            hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 2, MODE>), g, b, 0, s, a);
             return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
         }
+    } else {
+        // The residual form is compiled with streaming accesses only.
+        constexpr bool RES = MODE == FWD_RESIDUAL;
+        const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
+        if constexpr (NV <= 4) {
+            // short per-lane rows: a third row buffer is affordable
+            if (((p.flags >> 4) & 7) == 3) {
+                if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 3, MODE>), g, b, 0, s, a);
+                else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 3, MODE>), g, b, 0, s, a);
+                return hipGetLastError();
+            }
+        }
+        if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 2, MODE>), g, b, 0, s, a);
+        else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 2, MODE>), g, b, 0, s, a);
+        return hipGetLastError();
     }
-    if (nt) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, true, 2, RES>), g, b, 0, s, a);
-    else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_fwd<XT, WT, LPRC, NV, WGMAX, false, 2, false>), g, b, 0, s, a);
-    return hipGetLastError();
 }
 
 // (group class, vectors per lane, largest work-group) triples compiled.
@@ -185,28 +225,33 @@ bool fwd_variant_exists(int lprc, int nv, int wgs)
     return false;
 }
 
-template <int XT, int WT, bool RES>
+template <int XT, int WT, int MODE>
 static hipError_t fwd_dispatch(const FwdArgs& a, const Policy& p, hipStream_t s)
 {
     const int lprc = p.lpr < 64 ? p.lpr : 64;
-#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return fwd_go<XT, WT, C, N, W, RES>(a, p, s);
+#define X(C, N, W) if (lprc == C && p.nv == N && p.wgs <= W) return fwd_go<XT, WT, C, N, W, MODE>(a, p, s);
     RN_FWD_VARIANTS(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-template <bool RES>
+template <int MODE>
 static hipError_t fwd_dtypes(const FwdArgs& a, int x_dtype, int w_dtype, const Policy& p, hipStream_t s)
 {
-    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return fwd_dispatch<DT_BF16, DT_BF16, RES>(a, p, s);
-    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return fwd_dispatch<DT_BF16, DT_F32, RES>(a, p, s);
-    if (x_dtype == DT_F32 && w_dtype == DT_F32) return fwd_dispatch<DT_F32, DT_F32, RES>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_BF16) return fwd_dispatch<DT_BF16, DT_BF16, MODE>(a, p, s);
+    if (x_dtype == DT_BF16 && w_dtype == DT_F32) return fwd_dispatch<DT_BF16, DT_F32, MODE>(a, p, s);
+    if (x_dtype == DT_F32 && w_dtype == DT_F32) return fwd_dispatch<DT_F32, DT_F32, MODE>(a, p, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s)
+hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int mode, const Policy& p, hipStream_t s)
 {
-    return residual ? fwd_dtypes<true>(a, x_dtype, w_dtype, p, s) : fwd_dtypes<false>(a, x_dtype, w_dtype, p, s);
+    switch (mode) {
+    case FWD_PLAIN: return fwd_dtypes<FWD_PLAIN>(a, x_dtype, w_dtype, p, s);
+    case FWD_RESIDUAL: return fwd_dtypes<FWD_RESIDUAL>(a, x_dtype, w_dtype, p, s);
+    case FWD_HEADS: return fwd_dtypes<FWD_HEADS>(a, x_dtype, w_dtype, p, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 } // namespace rn

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -333,6 +334,7 @@ int fwd_common(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dty
     rn::FwdArgs a{};
     a.lpr = p.lpr;
     a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0;
+    a.heads = 1;
     a.x = x; a.ldx = ldx;
     a.u = u; a.ldu = ldu;
     a.h = h; a.ldh = ldh;
@@ -341,8 +343,28 @@ int fwd_common(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dty
     a.rstd = rstd;
     a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype)); a.eps = eps;
     clear_last_error();
-    if (rn::launch_fwd(a, x_dtype, w_dtype, residual ? 1 : 0, p, (hipStream_t)stream) != hipSuccess)
+    if (rn::launch_fwd(a, x_dtype, w_dtype, residual ? rn::FWD_RESIDUAL : rn::FWD_PLAIN, p, (hipStream_t)stream) !=
+        hipSuccess)
         return RN_ERR_LAUNCH;
+    return RN_OK;
+}
+
+// Extent of a per-head tensor: T tokens of `heads` rows of D elements.
+Extent heads_extent(const void* p, int64_t T, int64_t heads, int64_t D, int64_t ld_t, int64_t ld_h, int64_t esize)
+{
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return {b, b + (uintptr_t)(((T - 1) * ld_t + (heads - 1) * ld_h + D) * esize)};
+}
+
+// Strides of a per-head tensor: heads of one token do not overlap and lie
+// inside the token's stride; both strides are 16-byte multiples.
+int check_heads(const void* p, int64_t ld_t, int64_t ld_h, int64_t heads, int64_t D, int dt)
+{
+    if (!aligned(p, 16)) return RN_ERR_ALIGN;
+    const int64_t es = elem_bytes(dt);
+    if ((ld_h * es) % 16 != 0 || (ld_t * es) % 16 != 0) return RN_ERR_STRIDE;
+    if (heads > 1 && ld_h < D) return RN_ERR_STRIDE;
+    if (ld_t < (heads - 1) * ld_h + D) return RN_ERR_STRIDE;
     return RN_OK;
 }
 
@@ -515,6 +537,58 @@ int rmsnorm_fwd_residual(const void* x, int64_t ldx, const void* u, int64_t ldu,
                          int64_t H, float eps, void* stream)
 {
     return fwd_common(x, ldx, u, ldu, x_dtype, w, w_dtype, y, ldy, h_out, ldh, rstd, T, H, eps, stream, true);
+}
+
+int rmsnorm_fwd_heads(const void* x, int64_t ld_token, int64_t ld_head, int x_dtype, const void* w, int w_dtype,
+                      void* y, int64_t ldy_token, int64_t ldy_head, float* rstd, int64_t T, int64_t heads,
+                      int64_t head_dim, float eps, void* stream)
+{
+    if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
+    const int64_t D = head_dim;
+    int st;
+    if ((st = check_h(D, x_dtype)) != RN_OK) return st;
+    if (D / elems_per_chunk(x_dtype) > RN_HEADS_MAX_VECTORS) return RN_ERR_SHAPE;
+    if (T < 0 || heads < 1 || heads > 65535) return RN_ERR_SHAPE;
+    if (T * heads > (int64_t)INT32_MAX) return RN_ERR_SHAPE;
+    const int64_t rows = T * heads;
+    Policy p{};
+    if ((st = policy_fwd(rows, D, x_dtype, 1, &p)) != RN_OK) return st;
+    if (rows == 0) return RN_OK;
+    if (!x || !w || !y) return RN_ERR_NULL;
+    if ((st = check_heads(x, ld_token, ld_head, heads, D, x_dtype)) != RN_OK) return st;
+    if ((st = check_heads(y, ldy_token, ldy_head, heads, D, x_dtype)) != RN_OK) return st;
+    if (!aligned(w, 16) || (rstd && !aligned(rstd, 4))) return RN_ERR_ALIGN;
+    const int xb = elem_bytes(x_dtype);
+    const Extent ex = heads_extent(x, T, heads, D, ld_token, ld_head, xb);
+    const Extent ey = heads_extent(y, T, heads, D, ldy_token, ldy_head, xb);
+    const Extent ew = vec_extent(w, D, elem_bytes(w_dtype));
+    const bool in_place = x == y && ld_token == ldy_token && (heads == 1 || ld_head == ldy_head);
+    if (overlap(ey, ex) && !in_place) return RN_ERR_ALIAS;
+    if (overlap(ey, ew)) return RN_ERR_ALIAS;
+    if (rstd) {
+        const Extent er = vec_extent(rstd, rows, 4);
+        if (overlap(er, ex) || overlap(er, ey) || overlap(er, ew)) return RN_ERR_ALIAS;
+    }
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    if ((st = policy_fwd(rows, D, x_dtype, cu, &p)) != RN_OK) return st;
+    apply_override(0, rows, (int)(D / elems_per_chunk(x_dtype)), &p);
+    if (p.lpr >= 64) return RN_ERR_SHAPE;                 // only sub-wave row groups serve this form
+    log_policy("fwd_heads", rows, D, p);
+
+    rn::FwdArgs a{};
+    a.lpr = p.lpr;
+    a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0;
+    a.heads = (int)heads;
+    a.x = x; a.ldx = ld_token; a.ldxh = ld_head;
+    a.w = w;
+    a.y = y; a.ldy = ldy_token; a.ldyh = ldy_head;
+    a.rstd = rstd;
+    a.T = rows; a.H = (int)D; a.nch = (int)(D / elems_per_chunk(x_dtype)); a.eps = eps;
+    clear_last_error();
+    if (rn::launch_fwd(a, x_dtype, w_dtype, rn::FWD_HEADS, p, (hipStream_t)stream) != hipSuccess) return RN_ERR_LAUNCH;
+    return RN_OK;
 }
 
 int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype,

@@ -22,16 +22,24 @@ struct Policy {
 constexpr int RN_FLAG_NT = 1;    // non-temporal (streaming) loads and stores
 constexpr int RN_FLAG_ILV = 2;   // interleaved row order (see RowWalk)
 
+// Forward forms (kernel template argument and launch_fwd's `mode`).
+constexpr int FWD_PLAIN = 0;
+constexpr int FWD_RESIDUAL = 1;   // training forward with a residual stream
+constexpr int FWD_HEADS = 2;      // per-head rows (QK-norm)
+
 struct FwdArgs {
     int lpr;                     // lanes per row group (runtime for class 64)
     int interleave;              // RN_FLAG_ILV set in the policy
+    int heads;                   // per-head form: heads per token (rows = T * heads)
     const void* x; int64_t ldx;
+    int64_t ldxh;                // per-head form: element stride between heads of x
+    int64_t ldyh;                // per-head form: element stride between heads of y
     const void* u; int64_t ldu;  // residual form: the residual input
     void* h; int64_t ldh;        // residual form: h_new = x + u, rounded to x's dtype
     const void* w;
     void* y; int64_t ldy;
-    float* rstd;
-    int64_t T; int H; int nch;   // nch = H / elements-per-chunk
+    float* rstd;                 // per-head form: may be null (not stored)
+    int64_t T; int H; int nch;   // T = rows; nch = H / elements-per-chunk
     float eps;
 };
 
@@ -72,9 +80,9 @@ struct Fp8Args {
 };
 
 // Launchers return hipSuccess or the launch error.  They assume validated args.
-// residual != 0 selects the training-pair variants that also read u (forward)
-// or g_residual (backward).
-hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s);
+// mode: FWD_PLAIN, FWD_RESIDUAL (also reads u, writes h_new) or FWD_HEADS.
+// residual != 0 selects the backward that also reads g_residual.
+hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int mode, const Policy& p, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);

@@ -8,6 +8,7 @@
  *   add_rmsnorm_fp8_block_quant   residual add + RMSNorm + e4m3 1x128 block quant
  *   rmsnorm_fwd_residual          training forward with a residual stream
  *   rmsnorm_bwd_residual          its backward (adds the residual-stream gradient)
+ *   rmsnorm_fwd_heads             per-head RMSNorm (QK-norm) over (token, head) rows
  *
  * Conventions shared by every entry point
  *   - Every function is extern "C", never throws, never allocates device or
@@ -50,6 +51,8 @@
  *       strip-reduction backward.
  *   [M] miles-ext-kernels PR #15 (re-vendoring the Cake RMSNorm packages):
  *       Summary and Accuracy, the per-element dw budget against an FP64 sum.
+ *   [Q] FlashInfer PR #6332 (QKV projection + QK-RMSNorm + RoPE overlapped
+ *       with the Ulysses head exchange): Description, operator math.
  */
 #ifndef RMSNORM_GFX950_H
 #define RMSNORM_GFX950_H
@@ -77,6 +80,7 @@ typedef enum {
 typedef enum { RN_F32 = 0, RN_BF16 = 1 } rn_dtype;
 
 #define RN_MAX_H 32768
+#define RN_HEADS_MAX_VECTORS 128   /* rmsnorm_fwd_heads: head_dim <= 1024 bf16 / 512 fp32 */
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* rn_status_string(int status);
@@ -186,6 +190,32 @@ int rmsnorm_bwd_residual(const void* dy, int64_t lddy,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Per-head RMSNorm, e.g. the QK-norm of attention  ([Q] Description,
+ * operator math: an fp32 RMSNorm over each head's head_dim values with one
+ * shared [head_dim] weight for all heads of Q, or of K).
+ * Row (t, h), t < T, h < heads, is the head_dim values at
+ *   x + t*ld_token + h*ld_head        (element offsets)
+ * and is written to y + t*ldy_token + h*ldy_head; with r = t*heads + h,
+ *   rstd[r] = 1 / sqrt( (sum_j row_j^2) / head_dim + eps )   (fp32)
+ *   y_j     = round_dtype( row_j * rstd[r] * w[j] )
+ * exactly as rmsnorm_fwd computes one row.  Q and K of a fused [T, (q+k+v)]
+ * projection are two calls on column offsets of the same buffer.
+ *   x, y  x_dtype; head_dim a multiple of 8 (bf16) / 4 (fp32) and at most
+ *         RN_HEADS_MAX_VECTORS 16-byte vectors; ld_head >= head_dim when
+ *         heads > 1, ld_token >= (heads-1)*ld_head + head_dim, both strides
+ *         16-byte multiples (else RN_ERR_STRIDE); 1 <= heads <= 65535 and
+ *         T*heads < 2^31 (else RN_ERR_SHAPE).
+ *   y     may be exactly x with the same strides (in place); otherwise the
+ *         byte extents of x and y may not overlap (RN_ERR_ALIAS).
+ *   w     [head_dim] w_dtype.
+ *   rstd  [T*heads] fp32 output, token-major; may be NULL (not stored).
+ */
+int rmsnorm_fwd_heads(const void* x, int64_t ld_token, int64_t ld_head, int x_dtype,
+                      const void* w, int w_dtype,
+                      void* y, int64_t ldy_token, int64_t ldy_head, float* rstd,
+                      int64_t T, int64_t heads, int64_t head_dim, float eps, void* stream);
+
+/*
  * Fused residual add + RMSNorm + FP8 e4m3 1x128 block quant
  * ([F] description: Kernel and API; review thread on the scale layout).
  * bf16 only; H a multiple of 128.  Per row r:
@@ -221,8 +251,9 @@ int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx,
 
 /*
  * Host-only launch policy query (no HIP call; usable without a GPU).
- * op: 0 = forward, 1 = backward (plain and residual form), 2 = fused fp8
- * producer, 3 = forward with a residual stream.
+ * op: 0 = forward (also per-head, with T = tokens * heads and H = head_dim),
+ * 1 = backward (plain and residual form), 2 = fused fp8 producer, 3 = forward
+ * with a residual stream.
  * Fills out[0..6] = { lanes per row, 16-byte vectors per lane, threads per
  * work-group, work-groups (row chunks), rows per work-group pass, kernel id,
  * flags (bit 0: non-temporal streaming loads/stores) }

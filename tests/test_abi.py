@@ -216,3 +216,79 @@ def test_fp8_validation(rn):
     assert call(n=A + 16) == 7                     # normed overlaps x
     assert call(sc=C + 64) == 7                    # scales inside out
     assert call(r=A) == 7                          # residual is x
+
+
+@no_gpu
+def test_fwd_residual_validation(rn):
+    f = rn.lib.rmsnorm_fwd_residual
+    args = dict(x=A, ldx=256, u=A + 0x100000, ldu=256, xd=1, w=B, wd=1, y=C, ldy=256, h=C + 0x100000, ldh=256,
+                r=C + 0x200000, T=4, H=256)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["x"], a["ldx"], a["u"], a["ldu"], a["xd"], a["w"], a["wd"], a["y"], a["ldy"], a["h"], a["ldh"],
+                 a["r"], a["T"], a["H"], 1e-6, None)
+
+    assert call(xd=0, wd=1) == 3
+    assert call(H=250) == 2
+    assert call(T=0, x=None, u=None, w=None, y=None, h=None, r=None) == 0
+    assert call(u=None) == 1
+    assert call(h=None) == 1
+    assert call(u=A + 0x100008) == 4
+    assert call(ldh=250) == 5
+    assert call(h=A + 64) == 7                     # h_out overlaps x without being x
+    assert call(h=A + 0x100000 + 64) == 7          # h_out overlaps u without being u
+    assert call(h=A, ldh=264) == 7                 # x itself but another stride
+    assert call(y=A + 0x100000) == 7               # y overlaps u
+    assert call(h=C + 16) == 7                     # h_out overlaps y
+
+
+@no_gpu
+def test_bwd_residual_validation(rn):
+    f = rn.lib.rmsnorm_bwd_residual
+    args = dict(dy=A, lddy=256, x=A + 0x100000, ldx=256, xd=1, w=B, wd=1, rstd=B + 0x1000, g=A + 0x200000,
+                ldg=256, dx=C, lddx=256, dw=C + 0x100000, T=4, H=256, ws=C + 0x200000, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["dy"], a["lddy"], a["x"], a["ldx"], a["xd"], a["w"], a["wd"], a["rstd"], a["g"], a["ldg"],
+                 a["dx"], a["lddx"], a["dw"], a["T"], a["H"], 1, a["ws"], a["wsb"], None)
+
+    assert call(g=None) == 1
+    assert call(g=A + 0x200008) == 4
+    assert call(ldg=100) == 5
+    assert call(g=C + 64) == 7                     # g_residual overlaps dx without being dx
+    assert call(g=C, ldg=264) == 7                 # dx itself but another stride
+    assert call(dw=A + 0x200000 + 64) == 7         # dw inside g_residual
+
+
+@no_gpu
+def test_fwd_heads_validation(rn):
+    f = rn.lib.rmsnorm_fwd_heads
+    # fused [T, 3*32*128] bf16 projection: q band at A, token stride 12288, head stride 128
+    args = dict(x=A, ldt=12288, ldh=128, xd=1, w=B, wd=1, y=C, ldyt=4096, ldyh=128, r=C + 0x1000000, T=4,
+                nh=32, D=128)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["x"], a["ldt"], a["ldh"], a["xd"], a["w"], a["wd"], a["y"], a["ldyt"], a["ldyh"], a["r"],
+                 a["T"], a["nh"], a["D"], 1e-6, None)
+
+    assert call(xd=0, wd=1) == 3
+    assert call(D=100) == 2                        # not a vector multiple
+    assert call(D=2048) == 2                       # beyond 128 vectors
+    assert call(nh=0) == 2
+    assert call(T=1 << 26, nh=64) == 2             # T*heads beyond 2^31
+    assert call(T=0, x=None, w=None, y=None, r=None) == 0
+    assert call(y=None) == 1
+    assert call(x=A + 2) == 4
+    assert call(r=C + 0x1000002) == 4
+    assert call(ldh=100) == 5                      # heads overlap each other
+    assert call(ldh=132) == 5                      # 264 B: not a 16-byte multiple
+    assert call(ldt=4000) == 5                     # heads spill past the token stride
+    assert call(y=A + 16) == 7                     # y overlaps x without being x
+    assert call(y=A, ldyt=12288, ldyh=256) == 7    # x itself but other strides
+    assert call(r=C + 64) == 7                     # rstd inside y

@@ -94,4 +94,8 @@ CONFIGS = {
     # the training pair with a residual stream (x, u, dy, g_residual all standard normal)
     "res_bf16_T8192_H4096": Workload("res_bf16_T8192_H4096", 8192, 4096, "bf16", "bf16", residual=True,
                                      g_residual=True, seed=SEED_BASE + 700),
+    # per-head RMSNorm (QK-norm): a fused [T, 3 * 32 * 128] bf16 QKV projection output; the q and k
+    # weights are w[:128] and w[128:256]
+    "qk_bf16_T8192_32x128": Workload("qk_bf16_T8192_32x128", 8192, 3 * 32 * 128, "bf16", "bf16",
+                                     seed=SEED_BASE + 800),
 }
