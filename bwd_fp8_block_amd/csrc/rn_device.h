@@ -142,23 +142,23 @@ __device__ __forceinline__ float readlane_f32(float v, int lane)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// Sum over aligned groups of LPRC lanes (LPRC in {16, 32, 64}); every lane
-// of a group receives the same sum.  Must run with all 64 lanes active.
+// Sum over aligned groups of LPRC lanes (LPRC in {4, 8, 16, 32, 64}); every
+// lane of a group receives the same sum.  Must run with all 64 lanes active.
 template <int LPRC>
 __device__ __forceinline__ float group_sum(float v)
 {
-    static_assert(LPRC == 16 || LPRC == 32 || LPRC == 64, "group width");
+    static_assert(LPRC == 4 || LPRC == 8 || LPRC == 16 || LPRC == 32 || LPRC == 64, "group width");
     v += dpp_f32<DPP_QUAD_XOR1>(v);
     v += dpp_f32<DPP_QUAD_XOR2>(v);
-    v += dpp_f32<DPP_HALF_MIRROR>(v);
-    v += dpp_f32<DPP_ROW_MIRROR>(v);
+    if constexpr (LPRC >= 8) v += dpp_f32<DPP_HALF_MIRROR>(v);
+    if constexpr (LPRC >= 16) v += dpp_f32<DPP_ROW_MIRROR>(v);
     if constexpr (LPRC >= 32) v += swz_xor16(v);
     if constexpr (LPRC >= 64) v = readlane_f32(v, 0) + readlane_f32(v, 32);
     return v;
 }
 
 // Row-group geometry of a work-group.  LPRC is the compile-time class of the
-// group width: 16 or 32 (several rows per wavefront) or 64, meaning the group
+// group width: 4 .. 32 (several rows per wavefront) or 64, meaning the group
 // is lpr = 64 * wpr lanes wide (wpr whole wavefronts, wpr chosen at launch).
 template <int LPRC>
 struct Rows {

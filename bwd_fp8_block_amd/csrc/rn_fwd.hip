@@ -50,7 +50,6 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     const int nch = a.nch;
 
     const RowWalk W = row_walk(a.interleave != 0, xcd_chunk(blockIdx.x, gridDim.x), gridDim.x, a.T, gpw, R.grp);
-    const int n_it = W.n_it;
 
     // This lane's chunks: index (clamped into the row so that every load is
     // in bounds) and whether it is real.
@@ -78,11 +77,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     char* ybase = static_cast<char*>(a.y);
     char* hbase = static_cast<char*>(a.h);
 
-    // Rows of this group: lo + grp + it * gpw.  Past the end of the chunk the
-    // address is clamped to the chunk's last row (nothing is stored for it).
-    // Loaded registers are not touched until they are used, so the loads of
-    // the next row stay in flight while the current row is processed.
-    // Element offsets of row r in x and in y (and h_new, u).
+    // Element offsets of row r in x and in y (u and h_new use plain strides).
     auto xoff = [&](int64_t r) -> int64_t {
         if constexpr (HEADS) {
             const uint32_t rr = (uint32_t)r, t = rr / (uint32_t)a.heads;   // rows < 2^31 (host check)
@@ -100,6 +95,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
         }
     };
 
+    // Rows past the end of the walk load from a clamped in-bounds row and
+    // store nothing.  Loaded registers are not touched until they are used,
+    // so the next row's loads stay in flight while this row is processed.
     struct RowBuf {
         u32x4 v[NV];
         u32x4 u[RES ? NV : 1];
@@ -119,6 +117,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     auto process = [&](const RowBuf& b, int it) {
         // The row that is normalised: x, or h_new = round(x + u).
         u32x4 xv[NV];
+        float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             if constexpr (RES) {
@@ -131,21 +130,16 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
             } else {
                 xv[i] = b.v[i];
             }
-        }
-        const int64_t r = W.row(it);
-        const bool valid = W.valid(r);
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
             float f[E];
             unpack<XT>(keep_if(cok[i], xv[i]), f);      // clamped duplicate chunks add nothing
 #pragma unroll
             for (int e = 0; e < E; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
         }
         ss = R.sum(ss, red, it);
+        const int64_t r = W.row(it);
         const float ms = ss / (float)a.H;
         const float rs = 1.0f / __builtin_sqrtf(ms + a.eps);
-        if (valid) {
+        if (W.valid(r)) {
             u32x4* yrow = reinterpret_cast<u32x4*>(ybase + yoff(r) * XB);
             if constexpr (RES) {
                 u32x4* hrow = reinterpret_cast<u32x4*>(hbase + r * a.ldh * XB);
@@ -160,9 +154,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
                 opaque(xc);               // unpack again rather than keep E floats live
                 unpack<XT>(xc, f);
 #pragma unroll
-                for (int k = 0; k < WCH; ++k) {
-                    opaque(wr[i][k]);
-                    unpack<WT>(wr[i][k], wf + k * WPER);
+                for (int q = 0; q < WCH; ++q) {
+                    if constexpr (LPRC == 64 || NV * E > 32) opaque(wr[i][q]);   // short rows: w stays unpacked
+                    unpack<WT>(wr[i][q], wf + q * WPER);
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e) o[e] = (f[e] * rs) * wf[e];
@@ -174,7 +168,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 
     // PD row buffers in a ring: the next PD-1 rows' loads are in flight while
     // the current row is reduced and written.
-    row_pipeline<PD, RowBuf>(n_it, load, process);
+    row_pipeline<PD, RowBuf>(W.n_it, load, process);
 }
 
 // ---------------------------------------------------------------------------
@@ -213,7 +207,8 @@ static hipError_t fwd_go(const FwdArgs& a, const Policy& p, hipStream_t s)
 }
 
 // (group class, vectors per lane, largest work-group) triples compiled.
-#define RN_FWD_VARIANTS(X) X(16, 1, 256) X(16, 2, 256) X(16, 4, 256) X(32, 2, 256) X(32, 4, 256)         \
+#define RN_FWD_VARIANTS(X) X(4, 4, 256) X(8, 1, 256) X(8, 2, 256) X(8, 4, 256)                            \
+    X(16, 1, 256) X(16, 2, 256) X(16, 4, 256) X(32, 2, 256) X(32, 4, 256)                                \
     X(64, 1, 256) X(64, 2, 256) X(64, 3, 256) X(64, 4, 256) X(64, 5, 256) X(64, 6, 256) X(64, 7, 256) \
     X(64, 8, 256) X(64, 5, 512) X(64, 6, 512) X(64, 7, 512) X(64, 8, 512)
 

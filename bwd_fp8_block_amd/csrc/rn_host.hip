@@ -100,16 +100,30 @@ int elem_bytes(int dt) { return dt == RN_BF16 ? 2 : 4; }
 // ---------------------------------------------------------------------------
 
 // Forward.  Rows split over two wavefronts with at most 4-8 vectors of 16
-// bytes per lane, walked as one interleaved window.  Short rows use 16/32/64
-// lane groups; very long rows more wavefronts.  Work-groups per CU, measured
-// on MI355X (H = 2048 .. 5120): four while T is at most 48 rows per CU (T =
-// 8192: 0.95-0.97 of a same-traffic streaming copy), two beyond (T = 16384 ..
-// 65536: 0.94-0.97, where four fall to 0.87-0.94).
+// bytes per lane, walked as one interleaved window.  Short rows (up to 128
+// vectors) take sub-wavefront groups of 8 to 32 lanes with up to 4 vectors
+// per lane; very long rows more wavefronts.  Work-groups per CU, measured on
+// MI355X: for rows of 2-16 KiB four while T is at most 48 rows per CU (T =
+// 8192: 0.95-0.97 of a same-traffic streaming copy) and two beyond (T =
+// 16384 .. 65536: 0.94-0.97, where four fall to 0.87-0.94); for short rows
+// (H = 128 .. 1024, T = 65536 .. 2^21) four up to 512 rows per CU (0.96-1.0),
+// beyond that eight for 8-lane groups and two for 16/32-lane groups
+// (0.85-0.95).
+int fwd_per_cu(int64_t T, int cu, const Policy& p)
+{
+    const bool long_run = T > 512 * (int64_t)cu;
+    if (p.lpr <= 8) return long_run ? 8 : 4;
+    if (p.lpr < 64) return long_run ? 2 : 4;
+    if (p.nv <= 4) return T <= 48 * (int64_t)cu ? 4 : 2;
+    return 2;
+}
+
 int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int nch = (int)(H / elems_per_chunk(x_dtype));
-    if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
-    else if (nch <= 32)   { p->lpr = 16; p->nv = 2; }
+    if (nch <= 8)         { p->lpr = 8; p->nv = 1; }
+    else if (nch <= 16)   { p->lpr = 8; p->nv = 2; }
+    else if (nch <= 32)   { p->lpr = 8; p->nv = 4; }
     else if (nch <= 64)   { p->lpr = 16; p->nv = 4; }
     else if (nch <= 128)  { p->lpr = 32; p->nv = 4; }
     else if (nch <= 256)  { p->lpr = 64; p->nv = (int)ceil_div(nch, 64); }
@@ -118,7 +132,7 @@ int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     if (p->lpr > 512) return RN_ERR_SHAPE;
     p->wgs = wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
-    const int64_t per_cu = p->nv <= 4 ? (T <= 48 * (int64_t)cu ? 4 : 2) : 2;
+    const int64_t per_cu = fwd_per_cu(T, cu, *p);
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
@@ -137,7 +151,8 @@ int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int st = policy_fwd(T, H, x_dtype, cu, p);
     if (st != RN_OK) return st;
-    const int64_t per_cu = (p->nv <= 4 && T <= 64 * (int64_t)cu) ? 2 : 1;
+    const int64_t per_cu = p->lpr < 64 ? std::max(1, fwd_per_cu(T, cu, *p) / 2)
+                         : (p->nv <= 4 && T <= 64 * (int64_t)cu) ? 2 : 1;
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
@@ -209,7 +224,7 @@ void apply_override(int op, int64_t T, int nch, Policy* p)
     else q.wgs = wgs_for(q.lpr, op == 1 ? 1024 : 256);
     if (q.lpr <= 0 || q.wgs <= 0 || q.wgs > 1024 || q.wgs % q.lpr != 0) return;
     if (op == 2 && q.lpr % 16 != 0) return;
-    if (q.lpr != 16 && q.lpr != 32 && q.lpr % 64 != 0) return;
+    if (q.lpr != 16 && q.lpr != 32 && q.lpr % 64 != 0 && !(op == 0 && (q.lpr == 4 || q.lpr == 8))) return;
     if ((int64_t)q.lpr * q.nv < nch) return;
     q.gpw = q.wgs / q.lpr;
     const int lprc = q.lpr < 64 ? q.lpr : 64;

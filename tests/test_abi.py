@@ -65,12 +65,14 @@ CU = 256
     (3, 8192, 4096, 1, 1), (3, 64, 256, 0, 0), (3, 5, 8, 1, 1), (3, 100, 120, 1, 1), (3, 33, 5120, 1, 0),
     (3, 17, 7168, 1, 1), (3, 9, 8200, 1, 1), (3, 5, 16384, 1, 1), (3, 3, 16384, 0, 0), (3, 2, 32768, 1, 1),
     (3, 1000, 128, 1, 1), (3, 300, 3072, 1, 1), (3, 7, 17408, 1, 1),
+    (0, 1 << 21, 128, 1, 1), (0, 65536, 256, 1, 1), (0, 262144, 512, 1, 1), (0, 65536, 1024, 1, 1),
+    (0, 65536, 64, 0, 0), (0, 9, 32, 0, 0),
 ])
 def test_policy_invariants(rn, op, T, H, xd, wd):
     p = rn.rn_query_policy(op, T, H, xd, wd, CU)
     E = 8 if xd == 1 else 4
     nch = H // E
-    assert p["lpr"] in (16, 32) or p["lpr"] % 64 == 0
+    assert p["lpr"] in ((8, 16, 32) if op in (0, 3) else (16, 32)) or p["lpr"] % 64 == 0
     assert p["lpr"] * p["nv"] >= nch                         # every chunk owned by a lane
     assert p["lpr"] * (p["nv"] - 1) < nch                    # no fully idle vector slot
     assert p["wgs"] % p["lpr"] == 0 and p["wgs"] <= 1024 and p["gpw"] == p["wgs"] // p["lpr"]
@@ -80,7 +82,8 @@ def test_policy_invariants(rn, op, T, H, xd, wd):
     # a compiled variant serves it: the same check the library applies to overrides
     lprc = min(p["lpr"], 64)
     if op in (0, 2, 3):
-        assert (lprc, p["nv"]) in {(16, 1), (16, 2), (16, 4), (32, 1), (32, 2), (32, 4)} or \
+        assert (lprc, p["nv"]) in {(4, 4), (8, 1), (8, 2), (8, 4), (16, 1), (16, 2), (16, 4), (32, 1), (32, 2),
+                                   (32, 4)} or \
             (lprc == 64 and (p["wgs"] <= 256 and 1 <= p["nv"] <= 8 or p["wgs"] <= 512 and 5 <= p["nv"] <= 8))
     else:
         assert (lprc, p["nv"]) in {(16, 1), (32, 1), (64, 1), (64, 2)}
@@ -98,6 +101,8 @@ def test_policy_shapes_of_the_workloads(rn):
     r = rn.rn_query_policy(3, 8192, 4096, 1, 1, CU)
     assert r["lpr"] == 128 and r["nv"] == 4 and r["grid"] == 512 and r["flags"] & 3 == 3
     assert rn.rn_query_policy(0, 65536, 4096, 1, 1, CU)["grid"] == 512
+    qk = rn.rn_query_policy(0, 8192 * 32, 128, 1, 1, CU)           # per-head rows of 128 bf16
+    assert qk["lpr"] == 8 and qk["nv"] == 2 and qk["grid"] == 2048
     assert rn.rn_query_policy(3, 65536, 4096, 1, 1, CU)["grid"] == 256
 
 
