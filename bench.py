@@ -14,6 +14,10 @@ same way at the same shape and reported under "next_ops" (not part of value):
     rmsnorm_fwd_residual   (x, u -> y, h_new, rstd)      4*T*H*2 + 2*H + 4*T
     rmsnorm_bwd_residual   (dy, h_new, rstd, g_residual -> dx, dw)
                                                           4*T*H*2 + 2*H + 4*T + 4*H
+and the per-head QK-norm of T = 8192 tokens of a fused [T, 3*32*128] bf16
+QKV projection: two rmsnorm_fwd_heads calls (the q band and the k band, each
+its own [128] weight) into dense [T, 32, 128] outputs with rstd,
+    qk_norm                2 * (2*T*32*128*2 + 4*T*32 + 2*128)
 
 value = algorithmic bytes of a step / wall time per step (GB/s).  Algorithmic
 bytes count each tensor once (weight once, not per row):
@@ -44,7 +48,8 @@ KERNEL_SOURCES = {
 }
 KERNEL_NAMES = {"fwd": "k_rmsnorm_fwd", "bwd": "k_rmsnorm_bwd + k_dw_reduce", "fp8": "k_add_rmsnorm_fp8",
                 "fwd_residual": "k_rmsnorm_fwd (residual form)",
-                "bwd_residual": "k_rmsnorm_bwd (residual form) + k_dw_reduce"}
+                "bwd_residual": "k_rmsnorm_bwd (residual form) + k_dw_reduce",
+                "qk_norm": "k_rmsnorm_fwd (per-head form) x 2"}
 
 
 def algorithmic_bytes(T, H):
@@ -56,10 +61,14 @@ def algorithmic_bytes(T, H):
     }
 
 
+QK_HEADS, QK_DIM = 32, 128
+
+
 def next_bytes(T, H):
     return {
         "fwd_residual": 4 * T * H * 2 + 2 * H + 4 * T,
         "bwd_residual": 4 * T * H * 2 + 2 * H + 4 * T + 4 * H,
+        "qk_norm": 2 * (2 * T * QK_HEADS * QK_DIM * 2 + 4 * T * QK_HEADS + 2 * QK_DIM),
     }
 
 
@@ -134,30 +143,50 @@ def make_res_set(torch, gen, dev, T, H, rn):
     tmp = torch.empty(T, H, dtype=bf, device=dev)
     rn.rmsnorm_fwd_residual(randn(T, H), randn(T, H), s["w"], tmp, s["hb"], s["rb"], EPS)
     del tmp
+    # per-head QK-norm: q and k bands of a fused QKV projection output
+    nh, D = QK_HEADS, QK_DIM
+    s["qkv"] = randn(T, 3 * nh * D)
+    s["wq"] = (1.0 + 0.1 * torch.randn(D, generator=gen, device=dev)).to(bf)
+    s["wk"] = (1.0 + 0.1 * torch.randn(D, generator=gen, device=dev)).to(bf)
+    s["qo"] = torch.empty(T, nh, D, dtype=bf, device=dev)
+    s["ko"] = torch.empty(T, nh, D, dtype=bf, device=dev)
+    s["qr"] = torch.empty(T * nh, dtype=torch.float32, device=dev)
+    s["kr"] = torch.empty(T * nh, dtype=torch.float32, device=dev)
     return s
 
 
 def time_next(torch, rn, gen, dev, T, H, K, W):
-    """Per-launch times of the residual training pair (two alternating buffer sets)."""
+    """Per-launch times of the residual training pair and the QK-norm (two alternating buffer sets)."""
     sets = [make_res_set(torch, gen, dev, T, H, rn) for _ in range(2)]
+    nh, D = QK_HEADS, QK_DIM
+
+    def band(s, k):
+        return s["qkv"][:, k * nh * D:(k + 1) * nh * D].view(T, nh, D)
+
     plans = [(rn.plan_rmsnorm_fwd_residual(s["x"], s["u"], s["w"], s["y"], s["h"], s["r"], EPS),
               rn.plan_rmsnorm_bwd_residual(s["dy"], s["hb"], s["w"], s["rb"], s["gr"], s["dx"], s["dw"],
-                                           deterministic=True, workspace=s["ws"])) for s in sets]
+                                           deterministic=True, workspace=s["ws"]),
+              rn.plan_rmsnorm_fwd_heads(band(s, 0), s["wq"], s["qo"], s["qr"], EPS),
+              rn.plan_rmsnorm_fwd_heads(band(s, 1), s["wk"], s["ko"], s["kr"], EPS)) for s in sets]
     for i in range(W):
         for f in plans[i % 2]:
             f()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for i in range(K):
-        fwd, bwd = plans[i % 2]
+        fwd, bwd, qn, kn = plans[i % 2]
         evs[i][0].record()
         fwd()
         evs[i][1].record()
         bwd()
         evs[i][2].record()
+        qn()
+        kn()
+        evs[i][3].record()
     torch.cuda.synchronize()
     per = {"fwd_residual": sum(e[0].elapsed_time(e[1]) for e in evs) / K,
-           "bwd_residual": sum(e[1].elapsed_time(e[2]) for e in evs) / K}
+           "bwd_residual": sum(e[1].elapsed_time(e[2]) for e in evs) / K,
+           "qk_norm": sum(e[2].elapsed_time(e[3]) for e in evs) / K}
     b = next_bytes(T, H)
     out = {}
     for k, ms in per.items():
@@ -229,7 +258,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true", help="skip the residual training pair timing")
+    ap.add_argument("--no-next", action="store_true", help="skip the residual pair and QK-norm timing")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
