@@ -23,6 +23,9 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
+E4M3 = 0
+E5M2 = 1
 
 _lib = None
 
@@ -72,6 +75,19 @@ def _load():
     lib.rno_rmsnorm_bwd_residual.restype = i32
     lib.rno_rmsnorm_fwd_heads.argtypes = [vp, i64, i64, i32, vp, i32, i64, i64, i64, f32, vp, vp]
     lib.rno_rmsnorm_fwd_heads.restype = i32
+    lib.rno_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.rno_f16_to_double.restype = ctypes.c_double
+    lib.rno_double_to_f16.argtypes = [ctypes.c_double]
+    lib.rno_double_to_f16.restype = ctypes.c_uint16
+    lib.rno_e5m2_to_double.argtypes = [ctypes.c_uint8]
+    lib.rno_e5m2_to_double.restype = ctypes.c_double
+    lib.rno_float_to_e5m2.argtypes = [ctypes.c_float]
+    lib.rno_float_to_e5m2.restype = ctypes.c_uint8
+    lib.rno_quant_lp.argtypes = [vp, i64, i32, i32, i64, i64, f32, vp, i64, vp, i64]
+    lib.rno_quant_lp.restype = i32
+    lib.rno_add_rmsnorm_quant.argtypes = [vp, i64, vp, i64, vp, i32, i32, i64, i64, f32, f32,
+                                          vp, i64, vp, vp, i64, vp, i64, vp, i64, vp, i64]
+    lib.rno_add_rmsnorm_quant.restype = i32
     _lib = lib
     return lib
 
@@ -260,3 +276,64 @@ def rmsnorm_fwd_heads(x: np.ndarray, heads: int, head_dim: int, w: np.ndarray, e
     if rc:
         raise ValueError("oracle rmsnorm_fwd_heads rejected the arguments (%d)" % rc)
     return y, rstd
+
+
+def f16_to_double(b: int) -> float:
+    return _load().rno_f16_to_double(int(b))
+
+
+def double_to_f16(v: float) -> int:
+    return int(_load().rno_double_to_f16(float(v)))
+
+
+def e5m2_to_double(c: int) -> float:
+    return _load().rno_e5m2_to_double(int(c))
+
+
+def float_to_e5m2(v) -> int:
+    return int(_load().rno_float_to_e5m2(float(np.float32(v))))
+
+
+_FMT = {"e4m3": E4M3, "e5m2": E5M2}
+_LP = {"bf16": BF16, "f16": F16}
+
+
+def quant_lp(normed: np.ndarray, dtype: str, fmt: str, tensor_scale: float = 0.0, scale_ld: int | None = None):
+    """Codes of low-precision normed values (uint16 bits of bf16 or fp16, [T,H]).
+    tensor_scale > 0: that scale for every element (scale returned as None);
+    0: per-1x128-block scales amax/MAX (returned [H/128, scale_ld] float32, NaN padding)."""
+    lib = _load()
+    T, H = normed.shape
+    if scale_ld is None:
+        scale_ld = (T + 3) // 4 * 4
+    scale = None if tensor_scale else np.full((H // 128, scale_ld), np.nan, dtype=np.float32)
+    codes = np.empty((T, H), dtype=np.uint8)
+    rc = lib.rno_quant_lp(_ptr(normed), _row_stride(normed) if T else H, _LP[dtype], _FMT[fmt], T, H,
+                          np.float32(tensor_scale), _ptr(scale), scale_ld, _ptr(codes), H)
+    if rc:
+        raise ValueError("oracle quant_lp rejected the arguments (%d)" % rc)
+    return scale, codes
+
+
+def add_rmsnorm_quant(x: np.ndarray, res: np.ndarray, w: np.ndarray, eps: float, dtype: str, fmt: str,
+                      tensor_scale: float = 0.0, scale_ld: int | None = None):
+    """The producer variants (bf16 / fp16 rows as uint16 bits; e4m3 / e5m2 codes; block or given
+    per-tensor scale).  Returns dict h, rstd, normed (float64 unrounded), normed_lp (uint16 bits),
+    scale (None for a per-tensor scale), codes."""
+    lib = _load()
+    T, H = x.shape
+    if scale_ld is None:
+        scale_ld = (T + 3) // 4 * 4
+    h = np.empty((T, H), dtype=np.uint16)
+    rstd = np.empty((T,), dtype=np.float64)
+    normed = np.empty((T, H), dtype=np.float64)
+    nl = np.empty((T, H), dtype=np.uint16)
+    scale = None if tensor_scale else np.full((H // 128, scale_ld), np.nan, dtype=np.float32)
+    codes = np.empty((T, H), dtype=np.uint8)
+    rc = lib.rno_add_rmsnorm_quant(_ptr(x), _row_stride(x) if T else H, _ptr(res), _row_stride(res) if T else H,
+                                   _ptr(w), _LP[dtype], _FMT[fmt], T, H, np.float32(eps), np.float32(tensor_scale),
+                                   _ptr(h), H, _ptr(rstd), _ptr(normed), H, _ptr(nl), H,
+                                   _ptr(scale), scale_ld, _ptr(codes), H)
+    if rc:
+        raise ValueError("oracle add_rmsnorm_quant rejected the arguments (%d)" % rc)
+    return dict(h=h, rstd=rstd, normed=normed, normed_lp=nl, scale=scale, codes=codes)

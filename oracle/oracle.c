@@ -54,6 +54,11 @@
  *  R13 per-head RMSNorm treats every (token, head) slice of head_dim
  *      contiguous values as one row, with the same [head_dim] weight for all
  *      heads; rstd is indexed token-major, rstd[t*heads + h].
+ *  R14 producer variants: fp16 rows work as bf16 rows do (h, normed rounded
+ *      to fp16); an e5m2 output uses MAX = 57344 in place of 448 (scale =
+ *      amax / MAX); with a given per-tensor scale s every block uses s, and
+ *      codes = satfinite(n / s) (IEEE fp32 quotient, nearest-even, clamped
+ *      to +-MAX).
  */
 #include <math.h>
 #include <stddef.h>
@@ -63,6 +68,9 @@
 
 #define RNO_F32 0
 #define RNO_BF16 1
+#define RNO_F16 2
+#define RNO_E4M3 0
+#define RNO_E5M2 1
 
 /* ------------------------------------------------------------------------ */
 /* bf16 codec (bf16 = the upper 16 bits of an IEEE binary32).                */
@@ -442,5 +450,203 @@ int rno_rmsnorm_fwd_heads(const void* x, int64_t ld_token, int64_t ld_head, int 
             if (rc) return rc;
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 codec: 1 sign, 5 exponent (bias 15), 10 fraction bits;      */
+/* largest finite 65504; subnormals k * 2^-24.                               */
+/* ------------------------------------------------------------------------ */
+
+double rno_f16_to_double(uint16_t b)
+{
+    int neg = (b >> 15) & 1;
+    int ex = (b >> 10) & 0x1F;
+    int m = b & 0x3FF;
+    double v;
+    if (ex == 0x1F) return m ? NAN : (neg ? -INFINITY : INFINITY);
+    if (ex == 0)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp(1.0 + m / 1024.0, ex - 15);
+    return neg ? -v : v;
+}
+
+/* Round a double to the nearest binary16 value, ties to even, in one
+ * rounding; at or beyond the overflow threshold (65520) the result is +-inf. */
+uint16_t rno_double_to_f16(double v)
+{
+    if (isnan(v)) return 0x7E00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);               /* a in [2^(e-1), 2^e) */
+    int qexp = e - 11;                /* quantum of an 11-significant-bit value */
+    if (qexp < -24) qexp = -24;       /* subnormal quantum */
+    double quantum = ldexp(1.0, qexp);
+    double k = a / quantum;
+    double fl = floor(k);
+    double frac = k - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;
+    if (r >= 65536.0) return (uint16_t)(sign | 0x7C00);
+    if (r < ldexp(1.0, -14))          /* subnormal: r = m * 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    int er;
+    double f = frexp(r, &er);         /* r = (2f) * 2^(er-1), 2f in [1,2) */
+    int m = (int)((2.0 * f - 1.0) * 1024.0);
+    return (uint16_t)(sign | ((er - 1 + 15) << 10) | m);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E5M2 codec: 1 sign, 5 exponent (bias 15), 2 mantissa bits; S.11111.00 is  */
+/* infinity, S.11111.xx (xx != 0) NaN; largest finite 1.75 * 2^15 = 57344;   */
+/* subnormals k * 2^-16.                                                     */
+/* ------------------------------------------------------------------------ */
+
+double rno_e5m2_to_double(uint8_t c)
+{
+    int neg = (c >> 7) & 1;
+    int ex = (c >> 2) & 0x1F;
+    int m = c & 3;
+    double v;
+    if (ex == 0x1F) return m ? NAN : (neg ? -INFINITY : INFINITY);
+    if (ex == 0)
+        v = ldexp((double)m, -16);
+    else
+        v = ldexp(1.0 + m / 4.0, ex - 15);
+    return neg ? -v : v;
+}
+
+/* Round a binary32 value to E5M2, nearest-even, saturating to +-57344 (also
+ * for infinities); NaN gives 0x7F. */
+uint8_t rno_float_to_e5m2(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 57344.0) return (uint8_t)(sign | 0x7B);
+    int qexp;
+    if (a < ldexp(1.0, -14)) {
+        qexp = -16;                                /* subnormal spacing */
+    } else {
+        int e;
+        (void)frexp(a, &e);                        /* a in [2^(e-1), 2^e) */
+        qexp = e - 3;                              /* 3 significant bits */
+    }
+    double quantum = ldexp(1.0, qexp);
+    double k = a / quantum;
+    double fl = floor(k);
+    double frac = k - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;
+    if (r > 57344.0) r = 57344.0;
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -14)) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -16)));
+    int er;
+    double f = frexp(r, &er);
+    int m = (int)((2.0 * f - 1.0) * 4.0);
+    return (uint8_t)(sign | ((er - 1 + 15) << 2) | m);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Producer variants (reading R14): bf16 or fp16 rows, e4m3 or e5m2 codes,   */
+/* a dynamic scale per 1x128 block or one given per-tensor scale.            */
+/* FlashInfer PR #4480: description (the block-scaled sibling of the         */
+/* per-tensor FusedAddRMSNormQuant), its test matrix over fp16 and bf16      */
+/* inputs, and the review thread (the bound 448 tied to the output type,     */
+/* i.e. 57344 for e5m2).                                                     */
+/* ------------------------------------------------------------------------ */
+
+static double lp_decode(uint16_t b, int dtype)
+{
+    return dtype == RNO_F16 ? rno_f16_to_double(b) : rno_bf16_to_double(b);
+}
+
+static uint16_t lp_encode(double v, int dtype)
+{
+    return dtype == RNO_F16 ? rno_double_to_f16(v) : rno_double_to_bf16(v);
+}
+
+static uint8_t fp8_encode(float v, int fmt)
+{
+    return fmt == RNO_E5M2 ? rno_float_to_e5m2(v) : rno_float_to_e4m3(v);
+}
+
+static float fp8_max(int fmt) { return fmt == RNO_E5M2 ? 57344.0f : 448.0f; }
+
+/* Codes (and, with block scales, the scales) of low-precision normed values.
+ * tensor_scale > 0: one given scale for every element, no scales written;
+ * tensor_scale == 0: per row and 128-column block, s = amax / MAX. */
+int rno_quant_lp(const uint16_t* normed, int64_t ldn, int dtype, int fmt,
+                 int64_t T, int64_t H, float tensor_scale,
+                 float* scale, int64_t scale_ld,
+                 uint8_t* codes, int64_t ldq)
+{
+    if (T < 0 || H <= 0 || H % 128 != 0 || (tensor_scale == 0.0f && scale && scale_ld < T)) return 1;
+    if (tensor_scale < 0.0f || isnan(tensor_scale) || isinf(tensor_scale)) return 1;
+    float mx = fp8_max(fmt);
+    for (int64_t r = 0; r < T; ++r) {
+        for (int64_t k = 0; k < H / 128; ++k) {
+            float s = tensor_scale;
+            if (tensor_scale == 0.0f) {
+                float amax = 0.0f;
+                for (int64_t j = 128 * k; j < 128 * k + 128; ++j) {
+                    float a = (float)fabs(lp_decode(normed[r * ldn + j], dtype));
+                    if (a > amax) amax = a;
+                }
+                s = amax / mx;                              /* IEEE fp32 division */
+                if (scale) scale[k * scale_ld + r] = s;
+            }
+            if (!codes) continue;
+            for (int64_t j = 128 * k; j < 128 * k + 128; ++j) {
+                float n = (float)lp_decode(normed[r * ldn + j], dtype);
+                codes[r * ldq + j] = (s == 0.0f) ? 0x00 : fp8_encode(n / s, fmt);   /* IEEE fp32 division */
+            }
+        }
+    }
+    return 0;
+}
+
+/* The producer: h = round_lp(x + res) (written to h_out), rstd from h,
+ * n = h*rstd*w (FP64, unrounded to `normed`, rounded once to the row dtype
+ * in `normed_lp`), then rno_quant_lp of normed_lp.  Any output may be NULL. */
+int rno_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* res, int64_t ldr,
+                          const uint16_t* w, int dtype, int fmt,
+                          int64_t T, int64_t H, float eps, float tensor_scale,
+                          uint16_t* h_out, int64_t ldh, double* rstd,
+                          double* normed, int64_t ldn, uint16_t* normed_lp, int64_t ldnl,
+                          float* scale, int64_t scale_ld, uint8_t* codes, int64_t ldq)
+{
+    if (T < 0 || H <= 0 || H % 128 != 0) return 1;
+    if (dtype != RNO_BF16 && dtype != RNO_F16) return 1;
+    uint16_t* row = (uint16_t*)malloc((size_t)H * sizeof(uint16_t));
+    if (!row) return 2;
+    for (int64_t r = 0; r < T; ++r) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            uint16_t hb = lp_encode(lp_decode(x[r * ldx + j], dtype) + lp_decode(res[r * ldr + j], dtype), dtype);
+            if (h_out) h_out[r * ldh + j] = hb;
+            double hv = lp_decode(hb, dtype);
+            ss += hv * hv;
+        }
+        double rs = 1.0 / sqrt(ss / (double)H + (double)eps);
+        if (rstd) rstd[r] = rs;
+        for (int64_t j = 0; j < H; ++j) {
+            double hv = lp_decode(lp_encode(lp_decode(x[r * ldx + j], dtype) + lp_decode(res[r * ldr + j], dtype),
+                                            dtype), dtype);
+            double n = hv * rs * lp_decode(w[j], dtype);
+            if (normed) normed[r * ldn + j] = n;
+            row[j] = lp_encode(n, dtype);
+            if (normed_lp) normed_lp[r * ldnl + j] = row[j];
+        }
+        if (scale || codes) {
+            int rc = rno_quant_lp(row, H, dtype, fmt, 1, H, tensor_scale,
+                                  scale ? scale + r : NULL, scale_ld, codes ? codes + r * ldq : NULL, ldq);
+            if (rc) { free(row); return rc; }
+        }
+    }
+    free(row);
     return 0;
 }
