@@ -26,10 +26,15 @@ __all__ = [
     "plan_rmsnorm_fwd", "plan_rmsnorm_bwd", "plan_add_rmsnorm_fp8_block_quant",
     "rmsnorm_fwd_residual", "rmsnorm_bwd_residual", "plan_rmsnorm_fwd_residual", "plan_rmsnorm_bwd_residual",
     "rmsnorm_fwd_heads", "plan_rmsnorm_fwd_heads", "RN_HEADS_MAX_VECTORS",
+    "RN_F16", "RN_E4M3", "RN_E5M2", "add_rmsnorm_fp8_quant", "plan_add_rmsnorm_fp8_quant",
+    "rn_selftest_cvt_e5m2", "rn_selftest_quotient",
 ]
 
 RN_F32 = 0
 RN_BF16 = 1
+RN_F16 = 2
+RN_E4M3 = 0
+RN_E5M2 = 1
 RN_MAX_H = 32768
 RN_HEADS_MAX_VECTORS = 128
 
@@ -68,6 +73,13 @@ lib.rmsnorm_bwd_residual.restype = _i32
 lib.rmsnorm_fwd_heads.argtypes = [_vp, _i64, _i64, _i32, _vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                                   _f32, _vp]
 lib.rmsnorm_fwd_heads.restype = _i32
+lib.add_rmsnorm_fp8_quant.argtypes = [_vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i32, _vp, _i64, _vp, _vp, _i64,
+                                      _i64, _i64, _f32, _vp]
+lib.add_rmsnorm_fp8_quant.restype = _i32
+lib.rn_selftest_cvt_e5m2.argtypes = [_vp, _vp, _i64, _vp]
+lib.rn_selftest_cvt_e5m2.restype = _i32
+lib.rn_selftest_quotient.argtypes = [_i32, _i32, ctypes.c_uint32, ctypes.c_uint32, _vp, _i64, _vp, _vp, _vp]
+lib.rn_selftest_quotient.restype = _i32
 lib.rn_query_policy.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.rn_query_policy.restype = _i32
 lib.rn_bwd_workspace_bytes_for.argtypes = [_i64, _i64, _i32]
@@ -352,6 +364,65 @@ def rmsnorm_fwd_heads(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, rstd: t
     _check("rmsnorm_fwd_heads", st)
 
 
+_FP8_OUT = {torch.uint8: None, torch.float8_e4m3fn: RN_E4M3, torch.float8_e5m2: RN_E5M2}
+
+
+def _prep_fp8_quant(x, residual, w, out, block_scale, tensor_scale, normed_out, eps, out_format):
+    dev = _dev((x, residual, w, out, block_scale, tensor_scale, normed_out))
+    T, H = x.shape
+    if x.dtype == torch.bfloat16:
+        dt = RN_BF16
+    elif x.dtype == torch.float16:
+        dt = RN_F16
+    else:
+        raise ValueError("add_rmsnorm_fp8_quant: x must be bfloat16 or float16")
+    for t, n in ((residual, "residual"), (w, "w"), (normed_out, "normed_out")):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("%s must have x's dtype" % n)
+    if out.dtype not in _FP8_OUT:
+        raise ValueError("out must be uint8, float8_e4m3fn or float8_e5m2")
+    fmt = {"e4m3": RN_E4M3, "e5m2": RN_E5M2}[out_format] if isinstance(out_format, str) else int(out_format)
+    if _FP8_OUT[out.dtype] is not None and _FP8_OUT[out.dtype] != fmt:
+        raise ValueError("out's dtype does not match out_format")
+    if residual.shape != x.shape or out.shape != x.shape or w.shape != (H,) or \
+            (normed_out is not None and normed_out.shape != x.shape):
+        raise ValueError("add_rmsnorm_fp8_quant: shape mismatch")
+    if (block_scale is None) == (tensor_scale is None):
+        raise ValueError("give exactly one of block_scale and tensor_scale")
+    ps, sld, pt = None, 0, None
+    if block_scale is not None:
+        if block_scale.dtype != torch.float32 or block_scale.dim() != 2 or block_scale.shape[0] != H // 128:
+            raise ValueError("block_scale must be float32 [H/128, >= T]")
+        if block_scale.shape[1] < T or (block_scale.numel() > 1 and block_scale.stride(1) != 1):
+            raise ValueError("block_scale must be [H/128, ld >= T] with the row index contiguous")
+        ps = block_scale.data_ptr()
+        sld = block_scale.stride(0) if block_scale.shape[0] > 1 else block_scale.shape[1]
+    else:
+        if tensor_scale.dtype != torch.float32 or tensor_scale.numel() != 1:
+            raise ValueError("tensor_scale must be a one-element float32 device tensor")
+        pt = tensor_scale.data_ptr()
+    px, ldx = _mat(x, "x")
+    pr, ldr = _mat(residual, "residual")
+    po, ldo = _mat(out, "out")
+    pn, ldn = _mat(normed_out, "normed_out") if normed_out is not None else (None, 0)
+    with _on(dev):
+        args = (px, ldx, pr, ldr, _vec(w, "w"), dt, po, ldo, fmt, ps, sld, pt, pn, ldn, T, H, float(eps),
+                _stream(dev))
+    return dev, lib.add_rmsnorm_fp8_quant, args
+
+
+def add_rmsnorm_fp8_quant(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor, out: torch.Tensor,
+                          eps: float, out_format="e4m3", block_scale: torch.Tensor | None = None,
+                          tensor_scale: torch.Tensor | None = None, normed_out: torch.Tensor | None = None) -> None:
+    """Producer variants: bf16 or fp16 rows (x's dtype), e4m3 or e5m2 codes, and either
+    per-1x128-block scales (block_scale [H/128, ld]) or one given scale (tensor_scale, a
+    one-element float32 device tensor).  normed_out is optional."""
+    dev, fn, args = _prep_fp8_quant(x, residual, w, out, block_scale, tensor_scale, normed_out, eps, out_format)
+    with _on(dev):
+        st = fn(*args)
+    _check("add_rmsnorm_fp8_quant", st)
+
+
 def _plan(name, prep):
     dev, fn, args = prep
     cur = torch.cuda.current_device
@@ -397,6 +468,13 @@ def plan_rmsnorm_fwd_heads(x, w, y, rstd, eps):
     return _plan("rmsnorm_fwd_heads", _prep_fwd_heads(x, w, y, rstd, eps))
 
 
+def plan_add_rmsnorm_fp8_quant(x, residual, w, out, eps, out_format="e4m3", block_scale=None, tensor_scale=None,
+                               normed_out=None):
+    """Planned add_rmsnorm_fp8_quant (see plan_rmsnorm_fwd)."""
+    return _plan("add_rmsnorm_fp8_quant", _prep_fp8_quant(x, residual, w, out, block_scale, tensor_scale,
+                                                          normed_out, eps, out_format))
+
+
 def rn_query_policy(op: int, T: int, H: int, x_dtype: int, w_dtype: int, cu_count: int) -> dict:
     """Host-only launch policy (no GPU needed)."""
     out = (ctypes.c_int32 * 7)()
@@ -427,3 +505,24 @@ def rn_selftest_cvt_e4m3(x: torch.Tensor, out: torch.Tensor) -> None:
     with _on(dev):
         st = lib.rn_selftest_cvt_e4m3(x.data_ptr(), out.data_ptr(), x.numel(), _stream(dev))
     _check("rn_selftest_cvt_e4m3", st)
+
+
+def rn_selftest_cvt_e5m2(x: torch.Tensor, out: torch.Tensor) -> None:
+    """out[i] = e5m2 code of float32 x[i], via the producer's conversion instruction."""
+    dev = _dev((x, out))
+    if x.dtype != torch.float32 or out.dtype != torch.uint8 or x.numel() != out.numel():
+        raise ValueError("rn_selftest_cvt_e5m2: float32 in, uint8 out, same size")
+    with _on(dev):
+        st = lib.rn_selftest_cvt_e5m2(x.data_ptr(), out.data_ptr(), x.numel(), _stream(dev))
+    _check("rn_selftest_cvt_e5m2", st)
+
+
+def rn_selftest_quotient(dtype: int, out_format: int, mismatches: torch.Tensor, first_bad: torch.Tensor,
+                         a_lo: int = 0, a_hi: int = 0, scales: torch.Tensor | None = None) -> None:
+    """The producer's quotient against the IEEE division (see the C header)."""
+    dev = _dev((mismatches, first_bad, scales))
+    ps, ns = (scales.data_ptr(), scales.numel()) if scales is not None else (None, 0)
+    with _on(dev):
+        st = lib.rn_selftest_quotient(dtype, out_format, a_lo, a_hi, ps, ns, mismatches.data_ptr(),
+                                      first_bad.data_ptr(), _stream(dev))
+    _check("rn_selftest_quotient", st)

@@ -23,11 +23,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
 // Elements per 16-byte chunk for a storage dtype.
-template <int DT> struct Elems { static constexpr int value = (DT == DT_BF16) ? 8 : 4; };
+template <int DT> struct Elems { static constexpr int value = (DT == DT_F32) ? 4 : 8; };
 
 // ---------------------------------------------------------------------------
 // Global memory access.  NT selects non-temporal (streaming) hints.
@@ -77,6 +78,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     f32x2 v = {lo, hi};
     bf16x2 b = __builtin_convertvector(v, bf16x2);
     return __builtin_bit_cast(uint32_t, b);
+}
+
+// fp16 <-> fp32 (IEEE binary16; conversion to fp16 rounds to nearest even).
+__device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(f16x2, u)[0]; }
+__device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(f16x2, u)[1]; }
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    f16x2 h = __builtin_convertvector(v, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// 16-bit storage types by dtype: low / high half of a word, and packing.
+template <int DT> __device__ __forceinline__ float lo16(uint32_t u) { return DT == DT_F16 ? f16lo(u) : bf16lo(u); }
+template <int DT> __device__ __forceinline__ float hi16(uint32_t u) { return DT == DT_F16 ? f16hi(u) : bf16hi(u); }
+template <int DT> __device__ __forceinline__ uint32_t pack16x2(float lo, float hi)
+{
+    return DT == DT_F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
 }
 
 // Unpack one chunk of storage dtype DT into E fp32 values.

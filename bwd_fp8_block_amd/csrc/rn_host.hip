@@ -364,6 +364,67 @@ int fwd_common(const void* x, int64_t ldx, const void* u, int64_t ldu, int x_dty
     return RN_OK;
 }
 
+// The fused producer, every variant.
+// need_normed: normed_out is required (the block-quant entry point).
+int fp8_common(const void* x, int64_t ldx, void* residual, int64_t ldr, const void* w, int dtype, uint8_t* out,
+               int64_t ldo, int fmt, float* block_scale, int64_t scale_ld, const float* tensor_scale,
+               void* normed_out, int64_t ldn, int64_t T, int64_t H, float eps, void* stream, bool need_normed)
+{
+    if (dtype != RN_BF16 && dtype != RN_F16) return RN_ERR_DTYPE;
+    if (fmt != RN_E4M3 && fmt != RN_E5M2) return RN_ERR_DTYPE;
+    if (H <= 0 || H > RN_MAX_H || H % 128 != 0) return RN_ERR_SHAPE;
+    if (T < 0) return RN_ERR_SHAPE;
+    int st;
+    Policy p{};
+    if ((st = policy_fp8(T, H, 1, &p)) != RN_OK) return st;               // shape range (CU-independent)
+    if (T == 0) return RN_OK;
+    if (!x || !residual || !w || !out || (need_normed && !normed_out)) return RN_ERR_NULL;
+    const bool tsc = tensor_scale != nullptr;
+    if (tsc == (block_scale != nullptr)) return RN_ERR_NULL;              // exactly one scale form
+    if ((st = check_matrix(x, ldx, H, RN_BF16)) != RN_OK) return st;      // 16-bit rows either way
+    if ((st = check_matrix(residual, ldr, H, RN_BF16)) != RN_OK) return st;
+    if (normed_out && (st = check_matrix(normed_out, ldn, H, RN_BF16)) != RN_OK) return st;
+    if (!aligned(out, 16)) return RN_ERR_ALIGN;
+    if (ldo < H || ldo % 16 != 0) return RN_ERR_STRIDE;
+    if (!aligned(w, 16)) return RN_ERR_ALIGN;
+    if (tsc ? !aligned(tensor_scale, 4) : !aligned(block_scale, 4)) return RN_ERR_ALIGN;
+    if (!tsc && (scale_ld < T || scale_ld % 4 != 0)) return RN_ERR_STRIDE;
+    const Extent ex = mat_extent(x, T, H, ldx, 2), er = mat_extent(residual, T, H, ldr, 2);
+    const Extent ew = vec_extent(w, H, 2), eo = mat_extent(out, T, H, ldo, 1);
+    const Extent en = normed_out ? mat_extent(normed_out, T, H, ldn, 2) : Extent{0, 0};
+    const Extent es = tsc ? vec_extent(tensor_scale, 1, 4)
+                          : Extent{reinterpret_cast<uintptr_t>(block_scale),
+                                   reinterpret_cast<uintptr_t>(block_scale) + (uintptr_t)(((H / 128 - 1) * scale_ld + T) * 4)};
+    // Outputs: residual (in place), out, normed, and the block scales.  The
+    // per-tensor scale is an input: only the outputs may not overlap it.
+    if (overlap(er, ex) || overlap(er, ew) || overlap(eo, ex) || overlap(eo, er) || overlap(eo, ew) ||
+        overlap(eo, en) || overlap(eo, es) || overlap(en, ex) || overlap(en, er) || overlap(en, ew) ||
+        overlap(en, es) || overlap(es, er) || (!tsc && (overlap(es, ex) || overlap(es, ew))))
+        return RN_ERR_ALIAS;
+
+    int cu = 0;
+    if ((st = current_device_cu(&cu)) != RN_OK) return st;
+    if ((st = policy_fp8(T, H, cu, &p)) != RN_OK) return st;
+    apply_override(2, T, (int)(H / 8), &p);
+    log_policy("fp8", T, H, p);
+
+    rn::Fp8Args a{};
+    a.lpr = p.lpr;
+    a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0;
+    a.x = x; a.ldx = ldx;
+    a.res = residual; a.ldr = ldr;
+    a.w = w;
+    a.out = out; a.ldo = ldo;
+    a.scale = block_scale; a.scale_ld = scale_ld;
+    a.tscale = tensor_scale;
+    a.normed = normed_out; a.ldn = ldn;
+    a.T = T; a.H = (int)H; a.nch = (int)(H / 8); a.eps = eps;
+    clear_last_error();
+    if (rn::launch_fp8(a, dtype, fmt, tsc, p, (hipStream_t)stream) != hipSuccess)
+        return RN_ERR_LAUNCH;
+    return RN_OK;
+}
+
 // Extent of a per-head tensor: T tokens of `heads` rows of D elements.
 Extent heads_extent(const void* p, int64_t T, int64_t heads, int64_t D, int64_t ld_t, int64_t ld_h, int64_t esize)
 {
@@ -627,43 +688,17 @@ int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx, void* residual, int6
                                 uint8_t* out, int64_t ldo, float* block_scale, int64_t scale_ld, void* normed_out,
                                 int64_t ldn, int64_t T, int64_t H, float eps, void* stream)
 {
-    if (H <= 0 || H > RN_MAX_H || H % 128 != 0) return RN_ERR_SHAPE;
-    if (T < 0) return RN_ERR_SHAPE;
-    int st;
-    Policy p{};
-    if ((st = policy_fp8(T, H, 1, &p)) != RN_OK) return st;               // shape range (CU-independent)
-    if (T == 0) return RN_OK;
-    if (!x || !residual || !w || !out || !block_scale || !normed_out) return RN_ERR_NULL;
-    if ((st = check_matrix(x, ldx, H, RN_BF16)) != RN_OK) return st;
-    if ((st = check_matrix(residual, ldr, H, RN_BF16)) != RN_OK) return st;
-    if ((st = check_matrix(normed_out, ldn, H, RN_BF16)) != RN_OK) return st;
-    if (!aligned(out, 16)) return RN_ERR_ALIGN;
-    if (ldo < H || ldo % 16 != 0) return RN_ERR_STRIDE;
-    if (!aligned(w, 16) || !aligned(block_scale, 4)) return RN_ERR_ALIGN;
-    if (scale_ld < T || scale_ld % 4 != 0) return RN_ERR_STRIDE;
-    const Extent ex = mat_extent(x, T, H, ldx, 2), er = mat_extent(residual, T, H, ldr, 2);
-    const Extent ew = vec_extent(w, H, 2), eo = mat_extent(out, T, H, ldo, 1);
-    const Extent en = mat_extent(normed_out, T, H, ldn, 2);
-    const Extent es = {reinterpret_cast<uintptr_t>(block_scale),
-                       reinterpret_cast<uintptr_t>(block_scale) + (uintptr_t)(((H / 128 - 1) * scale_ld + T) * 4)};
-    if (overlap(er, ex) || overlap(er, ew) || overlap(eo, ex) || overlap(eo, er) || overlap(eo, ew) ||
-        overlap(eo, en) || overlap(eo, es) || overlap(en, ex) || overlap(en, er) || overlap(en, ew) ||
-        overlap(en, es) || overlap(es, ex) || overlap(es, er) || overlap(es, ew))
-        return RN_ERR_ALIAS;
+    return fp8_common(x, ldx, residual, ldr, w, RN_BF16, out, ldo, RN_E4M3, block_scale, scale_ld, nullptr,
+                      normed_out, ldn, T, H, eps, stream, true);
+}
 
-    int cu = 0;
-    if ((st = current_device_cu(&cu)) != RN_OK) return st;
-    if ((st = policy_fp8(T, H, cu, &p)) != RN_OK) return st;
-    apply_override(2, T, (int)(H / 8), &p);
-    log_policy("fp8", T, H, p);
-
-    rn::Fp8Args a{};
-    a.lpr = p.lpr; a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0; a.x = x; a.ldx = ldx; a.res = residual; a.ldr = ldr; a.w = w; a.out = out; a.ldo = ldo;
-    a.scale = block_scale; a.scale_ld = scale_ld; a.normed = normed_out; a.ldn = ldn;
-    a.T = T; a.H = (int)H; a.nch = (int)(H / 8); a.eps = eps;
-    clear_last_error();
-    if (rn::launch_fp8(a, p, (hipStream_t)stream) != hipSuccess) return RN_ERR_LAUNCH;
-    return RN_OK;
+int add_rmsnorm_fp8_quant(const void* x, int64_t ldx, void* residual, int64_t ldr, const void* w, int dtype,
+                          uint8_t* out, int64_t ldo, int out_format, float* block_scale, int64_t scale_ld,
+                          const float* tensor_scale, void* normed_out, int64_t ldn, int64_t T, int64_t H,
+                          float eps, void* stream)
+{
+    return fp8_common(x, ldx, residual, ldr, w, dtype, out, ldo, out_format, block_scale, scale_ld, tensor_scale,
+                      normed_out, ldn, T, H, eps, stream, false);
 }
 
 } // extern "C"

@@ -74,8 +74,9 @@ struct Fp8Args {
     void* res; int64_t ldr;
     const void* w;
     uint8_t* out; int64_t ldo;
-    float* scale; int64_t scale_ld;
-    void* normed; int64_t ldn;
+    float* scale; int64_t scale_ld;   // block scales (block-scale form)
+    const float* tscale;              // the given scale (per-tensor form)
+    void* normed; int64_t ldn;        // may be null in the general entry point
     int64_t T; int H; int nch;
     float eps;
 };
@@ -87,7 +88,9 @@ hipError_t launch_fwd(const FwdArgs& a, int x_dtype, int w_dtype, int mode, cons
 hipError_t launch_bwd(const BwdArgs& a, int x_dtype, int w_dtype, int residual, const Policy& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
-hipError_t launch_fp8(const Fp8Args& a, const Policy& p, hipStream_t s);
+// dtype DT_BF16 / DT_F16, fmt 0 = e4m3 / 1 = e5m2, tensor_scale: the given
+// per-tensor scale instead of block scales.
+hipError_t launch_fp8(const Fp8Args& a, int dtype, int fmt, bool tensor_scale, const Policy& p, hipStream_t s);
 
 // Variant tables (which (lpr, nv) pairs are compiled) -- used by the policy.
 // lprc is the group class: lpr for lpr < 64, else 64.

@@ -6,6 +6,8 @@
  *   rmsnorm_bwd                   dx and the fp32 weight gradient dw in one pass
  *                                 over the rows (fixed-order, repeatable dw)
  *   add_rmsnorm_fp8_block_quant   residual add + RMSNorm + e4m3 1x128 block quant
+ *   add_rmsnorm_fp8_quant         its variants: fp16 rows, e5m2 codes, or one
+ *                                 given per-tensor scale
  *   rmsnorm_fwd_residual          training forward with a residual stream
  *   rmsnorm_bwd_residual          its backward (adds the residual-stream gradient)
  *   rmsnorm_fwd_heads             per-head RMSNorm (QK-norm) over (token, head) rows
@@ -77,7 +79,8 @@ typedef enum {
     RN_ERR_LAUNCH = 9       /* the kernel launch failed (hipGetLastError)        */
 } rn_status;
 
-typedef enum { RN_F32 = 0, RN_BF16 = 1 } rn_dtype;
+typedef enum { RN_F32 = 0, RN_BF16 = 1, RN_F16 = 2 } rn_dtype;   /* RN_F16: the fp8 producer only */
+typedef enum { RN_E4M3 = 0, RN_E5M2 = 1 } rn_fp8_format;
 
 #define RN_MAX_H 32768
 #define RN_HEADS_MAX_VECTORS 128   /* rmsnorm_fwd_heads: head_dim <= 1024 bf16 / 512 fp32 */
@@ -250,6 +253,36 @@ int add_rmsnorm_fp8_block_quant(const void* x, int64_t ldx,
                                 int64_t T, int64_t H, float eps, void* stream);
 
 /*
+ * Producer variants  ([F] description: the block-scaled sibling of the
+ * per-tensor FusedAddRMSNormQuant, its tests over fp16 and bf16 inputs;
+ * review thread: the bound 448 belongs to e4m3 and follows the output type).
+ * As add_rmsnorm_fp8_block_quant, generalised:
+ *   dtype       RN_BF16 or RN_F16: x, residual, w and normed_out all have it;
+ *               h and n are rounded to it (nearest even).
+ *   out_format  RN_E4M3 (MAX = 448) or RN_E5M2 (MAX = 57344).
+ *   exactly one of
+ *     block_scale   block-scale form, as in add_rmsnorm_fp8_block_quant with
+ *                   s = a / MAX;
+ *     tensor_scale  per-tensor form: a DEVICE pointer to one fp32 scale s used
+ *                   for every element; codes = fp8(clamp(n / s, -MAX, MAX))
+ *                   with the IEEE fp32 quotient rounded to nearest even; no
+ *                   scales are written.  s must be a positive number (codes
+ *                   are 0x00 otherwise).  Both non-NULL or both NULL:
+ *                   RN_ERR_NULL.
+ *   normed_out  may be NULL (not written).
+ * With dtype RN_BF16, out_format RN_E4M3 and block_scale this computes what
+ * add_rmsnorm_fp8_block_quant computes, bit for bit.  Same limits and errors.
+ */
+int add_rmsnorm_fp8_quant(const void* x, int64_t ldx,
+                          void* residual, int64_t ldr,
+                          const void* w, int dtype,
+                          uint8_t* out, int64_t ldo, int out_format,
+                          float* block_scale, int64_t scale_ld,
+                          const float* tensor_scale,
+                          void* normed_out, int64_t ldn,
+                          int64_t T, int64_t H, float eps, void* stream);
+
+/*
  * Host-only launch policy query (no HIP call; usable without a GPU).
  * op: 0 = forward (also per-head, with T = tokens * heads and H = head_dim),
  * 1 = backward (plain and residual form), 2 = fused fp8 producer, 3 = forward
@@ -276,12 +309,27 @@ size_t rn_bwd_workspace_bytes_for(int64_t T, int64_t H, int cu_count);
  *   number of mismatching 8-value chunks to *d_mismatches and lowers
  *   *d_first_bad to (a << 16 | n-magnitude) of the first failure.  Both are
  *   device pointers the caller initialises.  Returns 0, 2 (bad range) or 9.
- * rn_selftest_cvt_e4m3: d_out[i] = e4m3 code of fp32 d_in[i] (i < n), made by
- *   the same conversion instruction the producer uses.  Returns 0, 1 or 9.
+ * rn_selftest_cvt_e4m3 / _e5m2: d_out[i] = e4m3 / e5m2 code of fp32 d_in[i]
+ *   (i < n), made by the same conversion instruction the producer uses.
+ *   Returns 0, 1 or 9.
+ * rn_selftest_quotient: the producer's quotient n / s against the IEEE fp32
+ *   division: the fp8 codes of the two for every pair, and the quotients bit
+ *   for bit wherever |n| >= 2^-100 and the IEEE quotient is a normal number
+ *   below 2 * MAX.
+ *   d_scales == NULL: block-scale form, for every amax pattern of `dtype` in
+ *   [a_lo, a_hi] (s = amax / MAX) and every n of that dtype with |n| <= amax;
+ *   otherwise per-tensor form, for each of the n_scales (<= 65535) device
+ *   scales and every finite n of the dtype.  Counts mismatches into
+ *   *d_mismatches and lowers *d_first_bad as rn_selftest_quant does.
+ *   Returns 0, 1, 2 (bad range), 3 (bad dtype or format) or 9.
  */
 int rn_selftest_quant(uint32_t a_lo, uint32_t a_hi, unsigned long long* d_mismatches,
                       uint32_t* d_first_bad, void* stream);
 int rn_selftest_cvt_e4m3(const float* d_in, uint8_t* d_out, int64_t n, void* stream);
+int rn_selftest_cvt_e5m2(const float* d_in, uint8_t* d_out, int64_t n, void* stream);
+int rn_selftest_quotient(int dtype, int out_format, uint32_t a_lo, uint32_t a_hi, const float* d_scales,
+                         int64_t n_scales, unsigned long long* d_mismatches, uint32_t* d_first_bad,
+                         void* stream);
 
 #ifdef __cplusplus
 }
