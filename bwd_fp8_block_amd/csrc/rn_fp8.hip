@@ -87,7 +87,7 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
 // The quotient of one element, as the codes use it.  fast: s >= 2^-100 (the
 // reciprocal r is finite).  Per-tensor form: quotients saturate at +-MAX, and
 // a nonzero |n| below 2^-100 takes the IEEE division (the FMA residual of the
-// correction could fall below the fp32 range there).
+// correction could fall below the fp32 range there; see tiny_n).
 template <int FMT, bool TSC>
 __device__ __forceinline__ float quot_elem(float n, float s, float r, bool fast)
 {
@@ -96,18 +96,21 @@ __device__ __forceinline__ float quot_elem(float n, float s, float r, bool fast)
     if (fast) {
         const float y = n * r;
         q = quot_fix(n, s, r, y);
-        if constexpr (TSC) {
-            const float an = __builtin_fabsf(n);
-            if (an < 0x1p-100f && an != 0.0f) q = n / s;
-            // |y| >= 2*MAX is far beyond saturation (and y may have overflowed)
+        if constexpr (TSC)   // |y| >= 2*MAX is far beyond saturation (and y may have overflowed)
             q = __builtin_fabsf(y) < 2.0f * MX ? __builtin_fminf(__builtin_fmaxf(q, -MX), MX)
                                                : __builtin_copysignf(MX, n);
-        }
     } else {
         q = n / s;
         if constexpr (TSC) q = __builtin_fminf(__builtin_fmaxf(q, -MX), MX);
     }
     return q;
+}
+
+// Per-tensor form: |n| nonzero and below 2^-100 (rare; handled off the fast path).
+__device__ __forceinline__ bool tiny_n(float n)
+{
+    const float an = __builtin_fabsf(n);
+    return an < 0x1p-100f && an != 0.0f;
 }
 
 // Codes of one 8-value chunk of 16-bit normed values (packed in nv) given
@@ -119,10 +122,21 @@ __device__ __forceinline__ u32x2 quant_chunk(const u32x4& nv, float s, float r_t
     const bool fast = s >= 0x1p-100f;
     const float r = TSC ? r_tensor : (fast ? recip_refined(s) : 0.0f);
     float q[8];
+    bool tiny = false;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const float n = (k & 1) ? hi16<XT>(nv[k >> 1]) : lo16<XT>(nv[k >> 1]);
         q[k] = quot_elem<FMT, TSC>(n, s, r, fast);
+        if constexpr (TSC) tiny |= tiny_n(n);
+    }
+    if constexpr (TSC) {
+        if (tiny && fast) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float n = (k & 1) ? hi16<XT>(nv[k >> 1]) : lo16<XT>(nv[k >> 1]);
+                if (tiny_n(n)) q[k] = quot_elem<FMT, TSC>(n, s, r, false);
+            }
+        }
     }
     u32x2 o;
     o[0] = cvt4<FMT>(q[0], q[1], q[2], q[3]);
@@ -397,7 +411,7 @@ __global__ __launch_bounds__(256) void k_quotient_selftest(uint32_t a_lo, const 
             const float n = DT == DT_F16 ? f16lo(b) : bf16lo(b);
             const float exact = n / s;                       // IEEE fp32 division
             const float ref = TSC ? __builtin_fminf(__builtin_fmaxf(exact, -MX), MX) : exact;
-            const float got = quot_elem<FMT, TSC>(n, s, r, fast);
+            const float got = quot_elem<FMT, TSC>(n, s, r, fast && !(TSC && tiny_n(n)));
             const float ae = __builtin_fabsf(exact);
             bool ok = cvt4<FMT>(got, 0.0f, 0.0f, 0.0f) == cvt4<FMT>(ref, 0.0f, 0.0f, 0.0f);
             if (__builtin_fabsf(n) >= 0x1p-100f && ae >= 0x1p-126f && ae < 2.0f * MX)

@@ -297,3 +297,28 @@ def test_fwd_heads_validation(rn):
     assert call(y=A + 16) == 7                     # y overlaps x without being x
     assert call(y=A, ldyt=12288, ldyh=256) == 7    # x itself but other strides
     assert call(r=C + 64) == 7                     # rstd inside y
+
+
+@no_gpu
+def test_fp8_quant_validation(rn):
+    f = rn.lib.add_rmsnorm_fp8_quant
+    args = dict(x=A, ldx=256, r=A + 0x100000, ldr=256, w=B, dt=2, out=C, ldo=256, fmt=1, sc=C + 0x100000, sld=8,
+                ts=None, n=C + 0x200000, ldn=256, T=4, H=256)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["x"], a["ldx"], a["r"], a["ldr"], a["w"], a["dt"], a["out"], a["ldo"], a["fmt"], a["sc"],
+                 a["sld"], a["ts"], a["n"], a["ldn"], a["T"], a["H"], 1e-6, None)
+
+    assert call(dt=0) == 3                         # fp32 rows are not a producer dtype
+    assert call(dt=7) == 3
+    assert call(fmt=2) == 3
+    assert call(H=200) == 2
+    assert call(T=0, x=None, r=None, w=None, out=None, sc=None, n=None) == 0
+    assert call(ts=B + 0x1000) == 1                # both scale forms
+    assert call(sc=None) == 1                      # neither
+    assert call(sc=None, ts=B + 0x1002) == 4       # misaligned per-tensor scale
+    assert call(sc=None, ts=C + 64) == 7           # per-tensor scale inside out
+    assert call(sld=3) == 5
+    assert call(n=A + 16) == 7
