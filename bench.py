@@ -18,6 +18,11 @@ and the per-head QK-norm of T = 8192 tokens of a fused [T, 3*32*128] bf16
 QKV projection: two rmsnorm_fwd_heads calls (the q band and the k band, each
 its own [128] weight) into dense [T, 32, 128] outputs with rstd,
     qk_norm                2 * (2*T*32*128*2 + 4*T*32 + 2*128)
+and two producer variants at T x H (add_rmsnorm_fp8_quant, normed written):
+    fp8_f16_e5m2_block     fp16 rows, e5m2 codes, block scales
+                                                          9*T*H + 2*H + 4*(H/128)*round_up(T,4)
+    fp8_bf16_e4m3_tensor   bf16 rows, e4m3 codes, one given scale
+                                                          9*T*H + 2*H + 4
 
 value = algorithmic bytes of a step / wall time per step (GB/s).  Algorithmic
 bytes count each tensor once (weight once, not per row):
@@ -49,7 +54,9 @@ KERNEL_SOURCES = {
 KERNEL_NAMES = {"fwd": "k_rmsnorm_fwd", "bwd": "k_rmsnorm_bwd + k_dw_reduce", "fp8": "k_add_rmsnorm_fp8",
                 "fwd_residual": "k_rmsnorm_fwd (residual form)",
                 "bwd_residual": "k_rmsnorm_bwd (residual form) + k_dw_reduce",
-                "qk_norm": "k_rmsnorm_fwd (per-head form) x 2"}
+                "qk_norm": "k_rmsnorm_fwd (per-head form) x 2",
+                "fp8_f16_e5m2_block": "k_add_rmsnorm_fp8 (fp16 rows, e5m2, block scales)",
+                "fp8_bf16_e4m3_tensor": "k_add_rmsnorm_fp8 (bf16 rows, e4m3, per-tensor scale)"}
 
 
 def algorithmic_bytes(T, H):
@@ -69,6 +76,8 @@ def next_bytes(T, H):
         "fwd_residual": 4 * T * H * 2 + 2 * H + 4 * T,
         "bwd_residual": 4 * T * H * 2 + 2 * H + 4 * T + 4 * H,
         "qk_norm": 2 * (2 * T * QK_HEADS * QK_DIM * 2 + 4 * T * QK_HEADS + 2 * QK_DIM),
+        "fp8_f16_e5m2_block": 9 * T * H + 2 * H + 4 * (H // 128) * ((T + 3) // 4 * 4),
+        "fp8_bf16_e4m3_tensor": 9 * T * H + 2 * H + 4,
     }
 
 
@@ -152,6 +161,18 @@ def make_res_set(torch, gen, dev, T, H, rn):
     s["ko"] = torch.empty(T, nh, D, dtype=bf, device=dev)
     s["qr"] = torch.empty(T * nh, dtype=torch.float32, device=dev)
     s["kr"] = torch.empty(T * nh, dtype=torch.float32, device=dev)
+    # producer variants
+    f16 = torch.float16
+    s["vx16"] = torch.randn(T, H, generator=gen, device=dev).to(f16)
+    s["vr16"] = torch.randn(T, H, generator=gen, device=dev).to(f16)
+    s["vw16"] = (1.0 + 0.1 * torch.randn(H, generator=gen, device=dev)).to(f16)
+    s["vn16"] = torch.empty(T, H, dtype=f16, device=dev)
+    s["vo"] = torch.empty(T, H, dtype=torch.uint8, device=dev)
+    s["vs"] = torch.empty(H // 128, (T + 3) // 4 * 4, dtype=torch.float32, device=dev)
+    s["vx"], s["vr"] = randn(T, H), randn(T, H)
+    s["vn"] = torch.empty(T, H, dtype=bf, device=dev)
+    s["vo2"] = torch.empty(T, H, dtype=torch.uint8, device=dev)
+    s["vts"] = torch.full((1,), 0.0125, dtype=torch.float32, device=dev)
     return s
 
 
@@ -167,14 +188,18 @@ def time_next(torch, rn, gen, dev, T, H, K, W):
               rn.plan_rmsnorm_bwd_residual(s["dy"], s["hb"], s["w"], s["rb"], s["gr"], s["dx"], s["dw"],
                                            deterministic=True, workspace=s["ws"]),
               rn.plan_rmsnorm_fwd_heads(band(s, 0), s["wq"], s["qo"], s["qr"], EPS),
-              rn.plan_rmsnorm_fwd_heads(band(s, 1), s["wk"], s["ko"], s["kr"], EPS)) for s in sets]
+              rn.plan_rmsnorm_fwd_heads(band(s, 1), s["wk"], s["ko"], s["kr"], EPS),
+              rn.plan_add_rmsnorm_fp8_quant(s["vx16"], s["vr16"], s["vw16"], s["vo"], EPS, out_format="e5m2",
+                                            block_scale=s["vs"], normed_out=s["vn16"]),
+              rn.plan_add_rmsnorm_fp8_quant(s["vx"], s["vr"], s["w"], s["vo2"], EPS, out_format="e4m3",
+                                            tensor_scale=s["vts"], normed_out=s["vn"])) for s in sets]
     for i in range(W):
         for f in plans[i % 2]:
             f()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     for i in range(K):
-        fwd, bwd, qn, kn = plans[i % 2]
+        fwd, bwd, qn, kn, v1, v2 = plans[i % 2]
         evs[i][0].record()
         fwd()
         evs[i][1].record()
@@ -183,10 +208,13 @@ def time_next(torch, rn, gen, dev, T, H, K, W):
         qn()
         kn()
         evs[i][3].record()
+        v1()
+        evs[i][4].record()
+        v2()
+        evs[i][5].record()
     torch.cuda.synchronize()
-    per = {"fwd_residual": sum(e[0].elapsed_time(e[1]) for e in evs) / K,
-           "bwd_residual": sum(e[1].elapsed_time(e[2]) for e in evs) / K,
-           "qk_norm": sum(e[2].elapsed_time(e[3]) for e in evs) / K}
+    keys = ["fwd_residual", "bwd_residual", "qk_norm", "fp8_f16_e5m2_block", "fp8_bf16_e4m3_tensor"]
+    per = {k: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / K for j, k in enumerate(keys)}
     b = next_bytes(T, H)
     out = {}
     for k, ms in per.items():
@@ -258,7 +286,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true", help="skip the residual pair and QK-norm timing")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the residual pair, QK-norm and producer-variant timings")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
