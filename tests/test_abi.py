@@ -322,3 +322,14 @@ def test_fp8_quant_validation(rn):
     assert call(sc=None, ts=C + 64) == 7           # per-tensor scale inside out
     assert call(sld=3) == 5
     assert call(n=A + 16) == 7
+
+
+def test_small_t_backward_is_one_strip_on_any_device(rn):
+    """Few rows: one row strip (one kernel, dw written directly), whatever the CU count, so
+    the bits of dw do not depend on the device; more rows: several strips."""
+    for T, H, d in ((1, 4096, 1), (4, 4096, 1), (8, 2048, 1), (64, 256, 0), (2, 7168, 1), (1, 16384, 1)):
+        grids = {rn.rn_query_policy(1, T, H, d, d, cu)["grid"] for cu in (8, 32, 80, 256, 304)}
+        assert grids == {1}, (T, H, grids)
+    for T, H, d in ((8, 4096, 1), (128, 256, 0), (300, 2048, 1)):
+        g = rn.rn_query_policy(1, T, H, d, d, 256)
+        assert g["grid"] > 1 and g["grid"] == rn.rn_query_policy(1, T, H, d, d, 304)["grid"]

@@ -168,6 +168,21 @@ def test_bwd_parity(rn, oracle, T, H, xd, wd, pad, det):
     check_dw(dw, dwref)
 
 
+@pytest.mark.parametrize("T,H,xd,wd", [(2, 4096, "bf16", "bf16"), (4, 4096, "bf16", "f32"), (5, 4096, "bf16", "bf16"),
+                                       (8, 2048, "bf16", "bf16"), (9, 2048, "bf16", "bf16"), (2, 7168, "bf16", "bf16"),
+                                       (16, 256, "f32", "f32"), (65, 256, "f32", "f32"), (1, 16384, "bf16", "bf16")])
+def test_bwd_small_t(rn, oracle, T, H, xd, wd):
+    """Around the one-strip threshold (one kernel writing dw directly below it)."""
+    d = generate(Workload("bwd_small", T, H, xd, wd, seed=2500 + T + H))
+    _, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6)
+    dx, dw = gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, True, poison=True)
+    dxref, dwref = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float64))
+    check_values("dx", dx, dxref, xd == "bf16")
+    check_dw(dw, dwref)
+    dx2, dw2 = gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, True)
+    assert np.array_equal(dw2.view(np.uint32), dw.view(np.uint32)) and np.array_equal(dx2, dx)
+
+
 def test_bwd_empty_sets_dw_zero(rn):
     H = 512
     dw = torch.full((H,), 7.0, device="cuda")
