@@ -30,7 +30,12 @@ bytes count each tensor once (weight once, not per row):
     bwd  3*T*H*2 + 2*H + 4*T + 4*H
     fp8  9*T*H + 2*H + 4*(H/128)*round_up(T,4)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next]
+`--latency` instead times single calls at few rows (the launch-bound regime,
+T = 1 .. 64): the fp32 T=64 H=256 workload and bf16 rows of H = 2048 / 4096,
+forward and backward, back to back on one stream, and prints one JSON line of
+microseconds per call (not the contract line).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next] [--latency]
 """
 import argparse
 import hashlib
@@ -225,6 +230,40 @@ def time_next(torch, rn, gen, dev, T, H, K, W):
     return out
 
 
+def latency(torch, rn, dev, K):
+    """Microseconds per call of back-to-back calls at few rows."""
+    def per_call(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / K, 3)
+
+    out = {}
+    empty = torch.zeros(1, device=dev)
+    out["empty_fill_kernel"] = per_call(lambda: empty.fill_(1.0))
+    for H, dt, Ts in ((256, torch.float32, (64,)), (2048, torch.bfloat16, (1, 8, 64)),
+                      (4096, torch.bfloat16, (1, 4, 64))):
+        for T in Ts:
+            x = torch.randn(T, H, device=dev).to(dt)
+            w = (1.0 + 0.1 * torch.randn(H, device=dev)).to(dt)
+            y, r = torch.empty_like(x), torch.empty(T, device=dev)
+            dy, dx = torch.randn(T, H, device=dev).to(dt), torch.empty_like(x)
+            dw = torch.empty(H, device=dev)
+            ws = torch.empty(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4 + 1, device=dev)
+            f = rn.plan_rmsnorm_fwd(x, w, y, r, EPS)
+            f()
+            b = rn.plan_rmsnorm_bwd(dy, x, w, r, dx, dw, True, ws)
+            key = "%s_T%d_H%d" % ("f32" if dt == torch.float32 else "bf16", T, H)
+            out[key] = {"fwd_us": per_call(f), "bwd_us": per_call(b)}
+    return out
+
+
 def run_step(calls, ev=None):
     fwd, bwd, fp8 = calls
     if ev is not None:
@@ -288,6 +327,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the residual pair, QK-norm and producer-variant timings")
+    ap.add_argument("--latency", action="store_true", help="time single calls at few rows instead")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
@@ -300,6 +340,9 @@ def main():
     import bwd_fp8_block_amd as rn
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.latency:
+        print(json.dumps({"latency_us_per_call": latency(torch, rn, dev, args.steps)}), flush=True)
+        return
     T, H = T_ROWS, HIDDEN
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261202)
