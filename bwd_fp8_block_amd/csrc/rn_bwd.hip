@@ -37,11 +37,26 @@
 
 namespace rn {
 
-// Workspace layout: column blocks of RN_PART_COLS columns; block b holds the
-// G strip partials of its columns contiguously, [b][strip][column % 16].
-__device__ __forceinline__ int64_t part_index(int64_t col, int64_t strip, int64_t G)
+// Workspace layout: one row of ldp = round_up(H, 16) fp32 partials per row
+// strip, [strip][column]; a lane writes its columns as whole 16-byte vectors.
+
+// E consecutive fp32 values to p: 16-byte stores when p allows them (the
+// workspace always does; dw itself, written directly by a single strip, need
+// only be 4-byte aligned).
+template <int E>
+__device__ __forceinline__ void store_floats(float* p, const float* v, bool vec)
 {
-    return ((col / RN_PART_COLS) * G + strip) * RN_PART_COLS + (col % RN_PART_COLS);
+    if (vec) {
+#pragma unroll
+        for (int k = 0; k < E; k += 4) {
+            u32x4 w = {__float_as_uint(v[k]), __float_as_uint(v[k + 1]), __float_as_uint(v[k + 2]),
+                       __float_as_uint(v[k + 3])};
+            *reinterpret_cast<u32x4*>(p + k) = w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k) p[k] = v[k];
+    }
 }
 
 template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, bool RES>
@@ -205,69 +220,62 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 
     // Emit this strip's dw partial: the gpw row groups' accumulators are
     // combined in a fixed order (group 0, 1, ...) in FP64 and rounded once to
-    // fp32.  Staged through LDS, HALF values per lane per pass.
-    float* part = a.part;
-    if (gpw == 1) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = lane + lpr * i;
-            if (c < nch) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float p = (float)acc[i][e];
-                    const int64_t col = (int64_t)c * E + e;
-                    part[part_index(col, strip, G)] = p;
-                }
-            }
-        }
-        return;
-    }
+    // fp32.  Groups 1.. stage their values through LDS, HALF per lane per
+    // pass; group 0 adds them to its own and writes whole vectors.
+    float* prow = a.part + strip * a.ldp;
+    const bool vec = a.part_vec != 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+        const int c = lane + lpr * i;
+        float outv[E];
+        if (gpw == 1) {
 #pragma unroll
-        for (int h0 = 0; h0 < E; h0 += HALF) {
+            for (int e = 0; e < E; ++e) outv[e] = (float)acc[i][e];
+        } else {
 #pragma unroll
-            for (int e = 0; e < HALF; ++e) stage[tid * HALF + e] = acc[i][h0 + e];
-            __syncthreads();
-            for (int v = tid; v < lpr * HALF; v += blockDim.x) {
-                const int l = v / HALF, e = v - l * HALF;
-                const int c = l + lpr * i;
-                if (c < nch) {
-                    double s = 0.0;
-                    for (int q = 0; q < gpw; ++q) s += stage[(q * lpr + l) * HALF + e];
-                    const float p = (float)s;
-                    const int64_t col = (int64_t)c * E + h0 + e;
-                    part[part_index(col, strip, G)] = p;
+            for (int h0 = 0; h0 < E; h0 += HALF) {
+                if (R.grp > 0) {
+#pragma unroll
+                    for (int e = 0; e < HALF; ++e) stage[tid * HALF + e] = acc[i][h0 + e];
                 }
+                __syncthreads();
+                if (R.grp == 0) {
+#pragma unroll
+                    for (int e = 0; e < HALF; ++e) {
+                        double s = 0.0 + acc[i][h0 + e];
+                        for (int q = 1; q < gpw; ++q) s += stage[(q * lpr + lane) * HALF + e];
+                        outv[h0 + e] = (float)s;
+                    }
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
+        if (R.grp == 0 && c < nch) store_floats<E>(prow + (int64_t)c * E, outv, vec);
     }
 }
 
 // dw[j] = fp32( sum over g = 0..G-1 of the strip partials of column j ), in
-// FP64 and a fixed order.  One work-group per block of 16 columns, whose G x 16
-// partials are contiguous.  Thread t owns column t % 16 and the strips
-// g = t/16, t/16 + 16, t/16 + 32, ... (summed in that order); the 16 sums of a
-// column are then added in the order t/16 = 0, 1, ..., 15.
+// FP64 and a fixed order.  One work-group per block of 16 columns.  Thread t
+// owns column t % 16 and the strips g = t/16, t/16 + 16, t/16 + 32, ...
+// (summed in that order; each g gives a 64-byte piece of a workspace row);
+// the 16 sums of a column are then added in the order t/16 = 0, 1, ..., 15.
 __global__ __launch_bounds__(256) void k_dw_reduce(ReduceArgs a)
 {
     __shared__ double red[16][16];
     const int t = threadIdx.x;
     const int c = t & 15, q = t >> 4;
-    const int64_t blk = blockIdx.x;
-    const float* p = a.part + blk * a.G * RN_PART_COLS;
+    const int64_t col0 = (int64_t)blockIdx.x * RN_PART_COLS;
+    const float* p = a.part + col0 + c;
     double s = 0.0;
 #pragma unroll 4
-    for (int64_t g = q; g < a.G; g += 16) s += (double)p[g * RN_PART_COLS + c];
+    for (int64_t g = q; g < a.G; g += 16) s += (double)p[g * a.ldp];
     red[q][c] = s;
     __syncthreads();
-    const int64_t col = blk * RN_PART_COLS + t;
-    if (t < 16 && col < a.H) {
+    if (t < 16 && col0 + t < a.H) {
         double u = 0.0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) u += red[k][t];
-        a.dw[col] = (float)u;
+        a.dw[col0 + t] = (float)u;
     }
 }
 
