@@ -24,8 +24,10 @@ and two producer variants at T x H (add_rmsnorm_fp8_quant, normed written):
     fp8_bf16_e4m3_tensor   bf16 rows, e4m3 codes, one given scale
                                                           9*T*H + 2*H + 4
 
-value = algorithmic bytes of a step / wall time per step (GB/s).  Algorithmic
-bytes count each tensor once (weight once, not per row):
+value = algorithmic bytes of a step / wall time per step (GB/s), timed over the
+K steps alone.  The per-op durations (and the roofline of the dominant kernel)
+come from HIP events around K back-to-back launches of each op right after.
+Algorithmic bytes count each tensor once (weight once, not per row):
     fwd  2*T*H*2 + 2*H + 4*T
     bwd  3*T*H*2 + 2*H + 4*T + 4*H
     fp8  9*T*H + 2*H + 4*(H/128)*round_up(T,4)
@@ -198,28 +200,10 @@ def time_next(torch, rn, gen, dev, T, H, K, W):
                                             block_scale=s["vs"], normed_out=s["vn16"]),
               rn.plan_add_rmsnorm_fp8_quant(s["vx"], s["vr"], s["w"], s["vo2"], EPS, out_format="e4m3",
                                             tensor_scale=s["vts"], normed_out=s["vn"])) for s in sets]
-    for i in range(W):
-        for f in plans[i % 2]:
-            f()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
-    for i in range(K):
-        fwd, bwd, qn, kn, v1, v2 = plans[i % 2]
-        evs[i][0].record()
-        fwd()
-        evs[i][1].record()
-        bwd()
-        evs[i][2].record()
-        qn()
-        kn()
-        evs[i][3].record()
-        v1()
-        evs[i][4].record()
-        v2()
-        evs[i][5].record()
-    torch.cuda.synchronize()
     keys = ["fwd_residual", "bwd_residual", "qk_norm", "fp8_f16_e5m2_block", "fp8_bf16_e4m3_tensor"]
-    per = {k: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / K for j, k in enumerate(keys)}
+    groups = {"fwd_residual": [0], "bwd_residual": [1], "qk_norm": [2, 3], "fp8_f16_e5m2_block": [4],
+              "fp8_bf16_e4m3_tensor": [5]}
+    per = {k: per_launch_ms(torch, [[pl[j] for j in groups[k]] for pl in plans], K) for k in keys}
     b = next_bytes(T, H)
     out = {}
     for k, ms in per.items():
@@ -264,19 +248,29 @@ def latency(torch, rn, dev, K):
     return out
 
 
-def run_step(calls, ev=None):
+def per_launch_ms(torch, calls_per_set, K):
+    """Average duration of one launch of an op (ms): K launches alternating the buffer
+    sets, back to back on torch's current stream (the stream the library launches on),
+    between two HIP events.  calls_per_set[i] is a list of callables (one op)."""
+    for i in range(4):
+        for f in calls_per_set[i % len(calls_per_set)]:
+            f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        for f in calls_per_set[i % len(calls_per_set)]:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def run_step(calls):
     fwd, bwd, fp8 = calls
-    if ev is not None:
-        ev[0].record()
     fwd()
-    if ev is not None:
-        ev[1].record()
     bwd()
-    if ev is not None:
-        ev[2].record()
     fp8()
-    if ev is not None:
-        ev[3].record()
 
 
 def cpu_baseline(T, H):
@@ -363,21 +357,18 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        run_step(plans[i % 2], evs[i])
+        run_step(plans[i % 2])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    per = {"fwd": 0.0, "bwd": 0.0, "fp8": 0.0}
-    for e in evs:
-        per["fwd"] += e[0].elapsed_time(e[1])
-        per["bwd"] += e[1].elapsed_time(e[2])
-        per["fp8"] += e[2].elapsed_time(e[3])
-    per = {k: v / K for k, v in per.items()}           # ms per launch
+    # Per-op launch durations (for the breakdown and the roofline), measured right
+    # after the timed steps on the same buffers: HIP events would add their own
+    # time to every step if recorded between the ops of the timed steps.
+    per = {k: per_launch_ms(torch, [[pl[j]] for pl in plans], K) for j, k in enumerate(("fwd", "bwd", "fp8"))}
     b = algorithmic_bytes(T, H)
     total = sum(b.values())
     value = total / (ms_per_step * 1e-3) / 1e9
