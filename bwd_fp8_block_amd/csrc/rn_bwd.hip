@@ -37,8 +37,15 @@
 
 namespace rn {
 
-// Workspace layout: one row of ldp = round_up(H, 16) fp32 partials per row
-// strip, [strip][column]; a lane writes its columns as whole 16-byte vectors.
+// Workspace layout: column blocks of RN_PART_COLS = 16 columns; block b holds
+// the G strip partials of its columns contiguously, [b][strip][column % 16],
+// so that the reduce reads each block as one contiguous run.  A lane's E
+// consecutive columns lie inside one block and are written as whole 16-byte
+// vectors.
+__device__ __forceinline__ int64_t part_index(int64_t col, int64_t strip, int64_t G)
+{
+    return ((col / RN_PART_COLS) * G + strip) * RN_PART_COLS + (col % RN_PART_COLS);
+}
 
 // E consecutive fp32 values to p: 16-byte stores when p allows them (the
 // workspace always does; dw itself, written directly by a single strip, need
@@ -222,7 +229,6 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     // combined in a fixed order (group 0, 1, ...) in FP64 and rounded once to
     // fp32.  Groups 1.. stage their values through LDS, HALF per lane per
     // pass; group 0 adds them to its own and writes whole vectors.
-    float* prow = a.part + strip * a.ldp;
     const bool vec = a.part_vec != 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -250,32 +256,33 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                 __syncthreads();
             }
         }
-        if (R.grp == 0 && c < nch) store_floats<E>(prow + (int64_t)c * E, outv, vec);
+        if (R.grp == 0 && c < nch) store_floats<E>(a.part + part_index((int64_t)c * E, strip, G), outv, vec);
     }
 }
 
 // dw[j] = fp32( sum over g = 0..G-1 of the strip partials of column j ), in
-// FP64 and a fixed order.  One work-group per block of 16 columns.  Thread t
-// owns column t % 16 and the strips g = t/16, t/16 + 16, t/16 + 32, ...
-// (summed in that order; each g gives a 64-byte piece of a workspace row);
-// the 16 sums of a column are then added in the order t/16 = 0, 1, ..., 15.
+// FP64 and a fixed order.  One work-group per block of 16 columns, whose G x 16
+// partials are contiguous.  Thread t owns column t % 16 and the strips
+// g = t/16, t/16 + 16, t/16 + 32, ... (summed in that order); the 16 sums of a
+// column are then added in the order t/16 = 0, 1, ..., 15.
 __global__ __launch_bounds__(256) void k_dw_reduce(ReduceArgs a)
 {
     __shared__ double red[16][16];
     const int t = threadIdx.x;
     const int c = t & 15, q = t >> 4;
-    const int64_t col0 = (int64_t)blockIdx.x * RN_PART_COLS;
-    const float* p = a.part + col0 + c;
+    const int64_t blk = blockIdx.x;
+    const float* p = a.part + blk * a.G * RN_PART_COLS;
     double s = 0.0;
 #pragma unroll 4
-    for (int64_t g = q; g < a.G; g += 16) s += (double)p[g * a.ldp];
+    for (int64_t g = q; g < a.G; g += 16) s += (double)p[g * RN_PART_COLS + c];
     red[q][c] = s;
     __syncthreads();
-    if (t < 16 && col0 + t < a.H) {
+    const int64_t col = blk * RN_PART_COLS + t;
+    if (t < 16 && col < a.H) {
         double u = 0.0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) u += red[k][t];
-        a.dw[col0 + t] = (float)u;
+        a.dw[col] = (float)u;
     }
 }
 

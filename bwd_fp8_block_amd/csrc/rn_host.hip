@@ -297,8 +297,7 @@ int check_h(int64_t H, int dt)
     return RN_OK;
 }
 
-// Workspace bytes for G row strips: one fp32 partial row of round_up(H, 16)
-// columns per strip.
+// Workspace bytes for G row strips: fp32 partials in blocks of 16 columns.
 size_t workspace_need(int64_t G, int64_t H)
 {
     const int64_t cols = (H + rn::RN_PART_COLS - 1) / rn::RN_PART_COLS * rn::RN_PART_COLS;
@@ -532,13 +531,11 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
     // straight into dw, with no second launch (the same bits as the reduce of
     // a single partial, which only widens it to FP64 and back).
     const bool direct = p.grid == 1;
-    const int64_t ldp = (H + rn::RN_PART_COLS - 1) / rn::RN_PART_COLS * rn::RN_PART_COLS;
     a.part = direct ? dw : static_cast<float*>(workspace);
-    a.ldp = ldp;
     a.part_vec = aligned(a.part, 16) ? 1 : 0;
     if (rn::launch_bwd(a, x_dtype, w_dtype, residual ? 1 : 0, p, s) != hipSuccess) return RN_ERR_LAUNCH;
     if (!direct) {
-        rn::ReduceArgs ra{static_cast<const float*>(workspace), dw, p.grid, (int)H, ldp};
+        rn::ReduceArgs ra{static_cast<const float*>(workspace), dw, p.grid, (int)H};
         if (rn::launch_bwd_reduce(ra, s) != hipSuccess) return RN_ERR_LAUNCH;
     }
     return RN_OK;

@@ -53,22 +53,19 @@ struct BwdArgs {
     const float* rstd;
     const void* gres; int64_t ldgr;   // residual form: gradient along the residual stream
     void* dx; int64_t lddx;
-    float* part;                 // one fp32 dw partial per (row strip, column): [strip][ldp]
-    int64_t ldp;                 // partial row stride (round_up(H, 16))
+    float* part;                 // one fp32 dw partial per (row strip, column), column-blocked
     int part_vec;                // part is 16-byte aligned (vector stores)
     int64_t T; int H; int nch;
     float inv_h;                 // 1/H rounded to fp32
 };
 
-// Partial rows are padded to a multiple of this many columns, the reduce's
-// column block (see rn_bwd.hip).
+// dw partials are stored in blocks of this many columns (see rn_bwd.hip).
 constexpr int RN_PART_COLS = 16;
 
 struct ReduceArgs {
-    const float* part;           // [G][ldp]
+    const float* part;           // [ceil(H/16)][G][16]
     float* dw;                   // [H]
     int64_t G; int H;
-    int64_t ldp;
 };
 
 struct Fp8Args {
