@@ -223,7 +223,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 
     // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in
     // flight while the current row is reduced and written.
-    row_pipeline<PD, RowBuf>(n_it, load, process);
+    row_pipeline<PD, true, RowBuf>(n_it, load, process);
 
     // Emit this strip's dw partial: the gpw row groups' accumulators are
     // combined in a fixed order (group 0, 1, ...) in FP64 and rounded once to
@@ -321,7 +321,7 @@ static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
 }
 
 // (group class, vectors per lane, largest work-group) triples compiled.
-#define RN_BWD_VARIANTS(X) X(16, 1, 1024) X(32, 1, 1024) X(64, 1, 1024) X(64, 2, 512) X(64, 2, 1024)
+#define RN_BWD_VARIANTS(X) X(16, 1, 1024) X(32, 1, 1024) X(64, 1, 512) X(64, 1, 1024) X(64, 2, 512) X(64, 2, 1024)
 
 bool bwd_variant_exists(int lprc, int nv, int wgs)
 {

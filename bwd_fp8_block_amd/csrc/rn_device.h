@@ -229,24 +229,55 @@ __device__ __forceinline__ uint32_t max16_u32(uint32_t v)
 }
 
 // Software pipeline over the rows of a row group: PD row buffers in a ring,
-// PD-1 rows of loads in flight while one row is processed.  All buffer
-// indices are compile-time constants after unrolling; the branches depend
-// only on n_it, which is uniform across the work-group, so `process` may
-// contain barriers.  load(buf, it) issues the loads of iteration `it`;
-// process(buf, it) consumes them.
-template <int PD, class Buf, class LoadF, class ProcF>
+// PD-1 rows of loads in flight while one row is processed.  load(buf, it)
+// issues the loads of iteration `it`; process(buf, it) consumes them.  All
+// buffer indices are compile-time constants after unrolling; the branches
+// depend only on n_it, which is uniform across the work-group, so `process`
+// may contain barriers.
+//
+// Two forms, which differ in where the compiler places its waits on the
+// vector-memory counter (computed per control-flow merge on gfx9):
+//   STEADY   whole blocks of PD iterations issue every prefetch
+//            unconditionally (iterations past n_it load the walk's clamped
+//            row, a real row, and are never processed); the last fewer than
+//            PD iterations follow without new loads.  Each row then waits
+//            only for its own loads: PD-1 rows stay in flight.
+//   guarded  a prefetch is issued only for a row that exists.  The merge
+//            after the guarded load makes the compiler's wait for the current
+//            row a drain of the prefetch and of earlier stores as well, so
+//            memory traffic advances about one row per row group at a time.
+// Which form streams faster depends on the kernel's mix of reads and writes
+// and on how many row groups share a CU; each kernel picks the one measured
+// faster on MI355X.
+template <int PD, bool STEADY, class Buf, class LoadF, class ProcF>
 __device__ __forceinline__ void row_pipeline(int n_it, LoadF&& load, ProcF&& process)
 {
     Buf b[PD];
+    if constexpr (STEADY) {
 #pragma unroll
-    for (int k = 0; k < PD - 1; ++k)
-        if (k < n_it) load(b[k], k);
-    for (int it = 0; it < n_it; it += PD) {
+        for (int k = 0; k < PD - 1; ++k) load(b[k], k);
+        int it = 0;
+        for (; it + PD <= n_it; it += PD) {
 #pragma unroll
-        for (int k = 0; k < PD; ++k) {
-            if (it + k < n_it) {
-                if (it + k + PD - 1 < n_it) load(b[(k + PD - 1) % PD], it + k + PD - 1);
+            for (int k = 0; k < PD; ++k) {
+                load(b[(k + PD - 1) % PD], it + k + PD - 1);
                 process(b[k], it + k);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PD - 1; ++k)
+            if (it + k < n_it) process(b[k], it + k);
+    } else {
+#pragma unroll
+        for (int k = 0; k < PD - 1; ++k)
+            if (k < n_it) load(b[k], k);
+        for (int it = 0; it < n_it; it += PD) {
+#pragma unroll
+            for (int k = 0; k < PD; ++k) {
+                if (it + k < n_it) {
+                    if (it + k + PD - 1 < n_it) load(b[(k + PD - 1) % PD], it + k + PD - 1);
+                    process(b[k], it + k);
+                }
             }
         }
     }
@@ -278,7 +309,8 @@ __device__ __forceinline__ void chunk_rows(int64_t g, int64_t G, int64_t T, int6
 
 // The rows a row group visits: row(it) = first + it * step for it < n_it;
 // rows at or past `limit` are padding (their loads use the clamped row
-// limit - 1, which is always a real row, and nothing is stored for them).
+// `last` = limit - 1, a real row since the grid never exceeds the row count
+// and so no chunk ends at row 0; nothing is stored for padding rows).
 //   contiguous:  work-group L owns the chunk [lo, hi) of rows; its gpw groups
 //                interleave inside it (first = lo + grp, step = gpw).
 //   interleaved: at iteration it the work-groups cover the rows
@@ -286,11 +318,11 @@ __device__ __forceinline__ void chunk_rows(int64_t g, int64_t G, int64_t T, int6
 //                the tensor as one moving window; L is XCD-aware, so each
 //                XCD's share of the window is contiguous.
 struct RowWalk {
-    int64_t first, step, limit;
+    int64_t first, step, limit, last;
     int n_it;
     __device__ __forceinline__ int64_t row(int it) const { return first + (int64_t)it * step; }
     __device__ __forceinline__ bool valid(int64_t r) const { return r < limit; }
-    __device__ __forceinline__ int64_t clamp(int64_t r) const { return r < limit ? r : limit - 1; }
+    __device__ __forceinline__ int64_t clamp(int64_t r) const { return r < limit ? r : last; }
 };
 
 __device__ __forceinline__ RowWalk row_walk(bool interleaved, int64_t L, int64_t G, int64_t T, int gpw, int grp)
@@ -309,6 +341,7 @@ __device__ __forceinline__ RowWalk row_walk(bool interleaved, int64_t L, int64_t
         w.limit = hi;
         w.n_it = (int)((hi - lo + gpw - 1) / gpw);
     }
+    w.last = w.limit > 0 ? w.limit - 1 : 0;
     return w;
 }
 

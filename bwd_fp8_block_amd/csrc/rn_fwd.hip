@@ -168,7 +168,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
 
     // PD row buffers in a ring: the next PD-1 rows' loads are in flight while
     // the current row is reduced and written.
-    row_pipeline<PD, RowBuf>(W.n_it, load, process);
+    row_pipeline<PD, false, RowBuf>(W.n_it, load, process);
 }
 
 // ---------------------------------------------------------------------------

@@ -162,10 +162,18 @@ int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 
 // Backward: one vector (8 bf16 / 4 fp32 columns) per lane so that the FP64
 // dw accumulators stay in registers; a row spans ceil(H/chunk/64) wavefronts;
-// one 1024-thread work-group (one row strip) per CU.  Rows wider than 1024
-// vectors take two vectors per lane.  The strip count depends only on T and
-// H while T is below one row per row group and CU, so for such T the bits
-// of dw do not depend on the device's CU count.
+// one work-group (one row strip) per CU.  Rows wider than 1024 vectors take
+// two vectors per lane.
+//   Few rows: 1024-thread groups, and a single strip that writes dw itself
+//   when each row group walks at most two rows (four for rows of at most 64
+//   vectors): measured on MI355X at 4.3-5.8 us against 6.5-7.3 us for two
+//   launches.  The strip count then depends only on T and H, so the bits of
+//   dw do not depend on the device's CU count.
+//   Streaming: rows of 64 to 512 lanes take 512-thread groups, wider rows one
+//   row per group, with three row buffers (two rows of loads in flight per
+//   row group).  Measured on MI355X against 1024-thread groups with two
+//   buffers: bf16 T=8192 H=4096 39.5 us vs 41.3 us, H=2048 T=58497 118 us vs
+//   125 us, H=5120 T=65536 353 us vs 403 us.
 int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int nch = (int)(H / elems_per_chunk(x_dtype));
@@ -174,20 +182,23 @@ int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     else if (nch <= 1024) { p->lpr = 64 * (int)ceil_div(nch, 64); p->nv = 1; }
     else                  { p->lpr = 64 * (int)ceil_div(nch, 128); p->nv = 2; }
     if (p->lpr > 1024) return RN_ERR_SHAPE;
-    p->wgs = wgs_for(p->lpr, 1024);
-    p->gpw = p->wgs / p->lpr;
-    int64_t g = ceil_div(T, p->gpw);
-    const int64_t per_cu = 1;
-    if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
-    // Few rows: one work-group walks them all and writes dw itself, saving
-    // the reduce launch (measured on MI355X: up to two rows per row group,
-    // or four for rows of at most 64 vectors, run in 4.3-5.8 us against
-    // 6.5-7.3 us for two launches).
-    const int64_t iters = ceil_div(T, p->gpw);
-    if (iters <= 2 || (iters <= 4 && nch <= 64)) g = 1;
-    p->grid = g < 1 ? 1 : g;
     p->kernel = 1;
     p->flags = RN_FLAG_NT_DEFAULT | rn::RN_FLAG_ILV;
+    p->wgs = wgs_for(p->lpr, 1024);
+    p->gpw = p->wgs / p->lpr;
+    const int64_t iters = ceil_div(T, p->gpw);
+    if (iters <= 2 || (iters <= 4 && nch <= 64)) {
+        p->grid = 1;
+        return RN_OK;
+    }
+    if (p->lpr >= 64 && p->nv == 1) {
+        p->wgs = wgs_for(p->lpr, 512);
+        p->gpw = p->wgs / p->lpr;
+        p->flags |= 3 << 4;                      // three row buffers
+    }
+    int64_t g = ceil_div(T, p->gpw);
+    if (g > (int64_t)cu) g = cu;
+    p->grid = g < 1 ? 1 : g;
     return RN_OK;
 }
 
