@@ -183,6 +183,22 @@ def test_bwd_small_t(rn, oracle, T, H, xd, wd):
     assert np.array_equal(dw2.view(np.uint32), dw.view(np.uint32)) and np.array_equal(dx2, dx)
 
 
+@pytest.mark.parametrize("T", [257, 511, 512, 513, 767, 769, 1024, 1025, 1279, 1793, 2048, 2049])
+def test_bwd_pipeline_tails(rn, oracle, T):
+    """Streaming backward with three row buffers: each strip walks ceil((T - s)/G) rows, so
+    these T give walks of 1 to 9 rows whose length modulo the ring size is 0, 1 and 2 (the
+    prefetch past the last row loads the clamped row and must change nothing)."""
+    H = 4096
+    pol = rn.rn_query_policy(1, T, H, 1, 1, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert pol["grid"] > 1 and (pol["flags"] >> 4) & 7 == 3, pol
+    d = generate(Workload("bwd_tails", T, H, "bf16", "bf16", seed=2700 + T))
+    _, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6)
+    dx, dw = gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, True, poison=True)
+    dxref, dwref = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float64))
+    check_values("dx", dx, dxref, True)
+    check_dw(dw, dwref)
+
+
 def test_bwd_empty_sets_dw_zero(rn):
     H = 512
     dw = torch.full((H,), 7.0, device="cuda")
