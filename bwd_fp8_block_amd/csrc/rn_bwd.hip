@@ -262,28 +262,48 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 
 // dw[j] = fp32( sum over g = 0..G-1 of the strip partials of column j ), in
 // FP64 and a fixed order.  One work-group per block of 16 columns, whose G x 16
-// partials are contiguous.  Thread t owns column t % 16 and the strips
-// g = t/16, t/16 + 16, t/16 + 32, ... (summed in that order); the 16 sums of a
-// column are then added in the order t/16 = 0, 1, ..., 15.
+// partials are contiguous.  Thread t reads 16-byte vectors (four columns,
+// quad t % 4) of the strips g = t/4, t/4 + 64, t/4 + 128, ... and adds them in
+// that order, issuing four loads before the first add (the partials were just
+// written by other CUs, so each round trip goes to memory); the 64 sums of a
+// column are then added as four runs of 16 (strip lanes 0-15, 16-31, ...) and
+// the four run totals in order.
 __global__ __launch_bounds__(256) void k_dw_reduce(ReduceArgs a)
 {
-    __shared__ double red[16][16];
+    __shared__ double red[64][RN_PART_COLS + 1];
+    __shared__ double red2[4][RN_PART_COLS];
     const int t = threadIdx.x;
-    const int c = t & 15, q = t >> 4;
+    const int cq = t & 3, sl = t >> 2;
     const int64_t blk = blockIdx.x;
-    const float* p = a.part + blk * a.G * RN_PART_COLS;
-    double s = 0.0;
-#pragma unroll 4
-    for (int64_t g = q; g < a.G; g += 16) s += (double)p[g * RN_PART_COLS + c];
-    red[q][c] = s;
+    const int64_t G = a.G;
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.part + blk * G * RN_PART_COLS) + cq;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    auto add = [&](const u32x4& v) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] += (double)__uint_as_float(v[k]);
+    };
+    int64_t g = sl;
+    for (; g + 192 < G; g += 256) {
+        const u32x4 v0 = p[g * 4], v1 = p[(g + 64) * 4], v2 = p[(g + 128) * 4], v3 = p[(g + 192) * 4];
+        add(v0);
+        add(v1);
+        add(v2);
+        add(v3);
+    }
+    for (; g < G; g += 64) add(p[g * 4]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[sl][cq * 4 + k] = acc[k];
     __syncthreads();
-    const int64_t col = blk * RN_PART_COLS + t;
-    if (t < 16 && col < a.H) {
+    if (t < 64) {
+        const int c = t & 15, run = t >> 4;
         double u = 0.0;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) u += red[k][t];
-        a.dw[col] = (float)u;
+        for (int k = 0; k < 16; ++k) u += red[run * 16 + k][c];
+        red2[run][c] = u;
     }
+    __syncthreads();
+    const int64_t col = blk * RN_PART_COLS + t;
+    if (t < 16 && col < a.H) a.dw[col] = (float)(((red2[0][t] + red2[1][t]) + red2[2][t]) + red2[3][t]);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t n)
