@@ -6,9 +6,11 @@
 //   xhat = x * rstd;  c = mean_j(g * w * xhat);  dx = rstd * (g*w - c*xhat)
 //   dw_j = sum over rows of g * x * rstd
 //
-// Mapping.  The rows are split into G contiguous chunks, one per work-group
-// ("strips").  A work-group holds GPW row groups of LPR lanes; each row group
-// walks every GPW-th row of the strip.  Per row: 16-byte loads of g and x,
+// Mapping.  The rows are split into G strips, one per work-group: a strip is
+// either a contiguous chunk of rows or, in the interleaved walk used for
+// streaming, every G-th block of GPW rows (all strips then move through the
+// tensor as one window).  A work-group holds GPW row groups of LPR lanes,
+// one row per group at a time.  Per row: 16-byte loads of g and x,
 // fp32 dot product reduced across the row group (DPP, then LDS when a row
 // spans several wavefronts), dx written back, and the dw contribution of the
 // row added to per-lane FP64 accumulators for the lane's columns.
@@ -221,8 +223,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         }
     };
 
-    // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in
-    // flight while the current row is reduced and written.
+    // PD row buffers in a ring, steady form: the g, x and rstd of the next
+    // PD-1 rows are in flight while the current row is reduced and written
+    // (the streaming launch uses PD = 3).
     row_pipeline<PD, true, RowBuf>(n_it, load, process);
 
     // Emit this strip's dw partial: the gpw row groups' accumulators are
