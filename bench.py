@@ -32,12 +32,16 @@ Algorithmic bytes count each tensor once (weight once, not per row):
     bwd  3*T*H*2 + 2*H + 4*T + 4*H
     fp8  9*T*H + 2*H + 4*(H/128)*round_up(T,4)
 
+`--ceiling` instead times plain streaming passes (rn_stream_mix) with each op's
+read:write mix and bytes at T x H, the best of a grid sweep, and prints one
+JSON line of them: the practical ceiling the op figures are compared with.
+
 `--latency` instead times single calls at few rows (the launch-bound regime,
 T = 1 .. 64): the fp32 T=64 H=256 workload and bf16 rows of H = 2048 / 4096,
 forward and backward, back to back on one stream, and prints one JSON line of
 microseconds per call (not the contract line).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next] [--latency]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next] [--latency] [--ceiling]
 """
 import argparse
 import hashlib
@@ -248,6 +252,48 @@ def latency(torch, rn, dev, K):
     return out
 
 
+# Practical ceilings: plain streaming passes with each op's read:write mix and
+# bytes at T x H (equal-size streams; the fp8 producer's 2 x T*H*2 read and
+# 2 x T*H*2 + T*H written bytes become 4 reads and 5 writes of T*H bytes).
+CEILING_MIXES = {
+    "fwd_1R1W": (1, 1, 2), "bwd_2R1W": (2, 1, 2), "fp8_4R5W": (4, 5, 1),
+    "fwd_residual_2R2W": (2, 2, 2), "bwd_residual_3R1W": (3, 1, 2),
+}
+
+
+def ceiling(torch, rn, dev, T, H, K):
+    """Per-call time of rn_stream_mix for each mix, best of a grid sweep; four
+    buffer sets alternate so that no pass finds its inputs in the Infinity Cache."""
+    out = {}
+    for name, (r, w, bytes_per_elem) in CEILING_MIXES.items():
+        nb = T * H * bytes_per_elem
+        sets = [([torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(r)],
+                 [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(w)]) for _ in range(4)]
+        for src, _ in sets:
+            for t in src:
+                t.fill_(1)
+        best = None
+        for grid in (512, 1024, 2048, 4096, 8192):
+            for k in range(8):
+                rn.rn_stream_mix(*sets[k % 4], grid)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(K):
+                rn.rn_stream_mix(*sets[k % 4], grid)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / K
+            if best is None or us < best[1]:
+                best = (grid, us)
+        total = (r + w) * nb
+        out[name] = {"bytes": total, "best_grid": best[0], "us": round(best[1], 2),
+                     "GB/s": round(total / best[1] / 1e3, 1), "pct_of_peak": round(100 * total / best[1] / 1e3 / HBM_PEAK_GBS, 2)}
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def per_launch_ms(torch, calls_per_set, K):
     """Average duration of one launch of an op (ms): K launches alternating the buffer
     sets, back to back on torch's current stream (the stream the library launches on),
@@ -322,6 +368,8 @@ def main():
     ap.add_argument("--no-next", action="store_true",
                     help="skip the residual pair, QK-norm and producer-variant timings")
     ap.add_argument("--latency", action="store_true", help="time single calls at few rows instead")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time plain streaming passes with each op's read:write mix instead (practical ceiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
@@ -336,6 +384,10 @@ def main():
     torch.cuda.set_device(dev)
     if args.latency:
         print(json.dumps({"latency_us_per_call": latency(torch, rn, dev, args.steps)}), flush=True)
+        return
+    if args.ceiling:
+        print(json.dumps({"stream_mix_ceiling_T%d_H%d" % (T_ROWS, HIDDEN):
+                          ceiling(torch, rn, dev, T_ROWS, HIDDEN, min(args.steps, 40))}), flush=True)
         return
     T, H = T_ROWS, HIDDEN
     gen = torch.Generator(device=dev)

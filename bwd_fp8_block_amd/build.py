@@ -1,6 +1,8 @@
 """Build the gfx950 HIP library librmsnorm_gfx950.so in-tree with hipcc.
 
-Usage: python -m bwd_fp8_block_amd.build   (or call build()).
+Usage: python bwd_fp8_block_amd/build.py   (or call build()).  Run it as a
+file, not as `-m bwd_fp8_block_amd.build`: the package's __init__ loads the
+library this script builds.  It imports only the standard library.
 """
 from __future__ import annotations
 
@@ -13,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librmsnorm_gfx950.so")
-SOURCES = ["rn_host.hip", "rn_fwd.hip", "rn_bwd.hip", "rn_fp8.hip"]
+SOURCES = ["rn_host.hip", "rn_fwd.hip", "rn_bwd.hip", "rn_fp8.hip", "rn_probe.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for every kernel.

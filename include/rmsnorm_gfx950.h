@@ -331,6 +331,23 @@ int rn_selftest_quotient(int dtype, int out_format, uint32_t a_lo, uint32_t a_hi
                          int64_t n_scales, unsigned long long* d_mismatches, uint32_t* d_first_bad,
                          void* stream);
 
+/*
+ * Measurement hook, not part of the RMSNorm path: the practical-ceiling
+ * probe that the kernels' bandwidth is compared with.  One grid-stride pass
+ * over n16 16-byte vectors: vector i of each of the nsrc source streams is
+ * read (non-temporal), the reads are combined with XOR and the result is
+ * written (non-temporal) to vector i of each of the ndst destination
+ * streams, so the pass moves (nsrc + ndst) * 16 * n16 bytes with that
+ * read:write mix and no other work.  (nsrc, ndst) is one of (1,1), (2,1),
+ * (3,1), (2,2), (4,5).  Every stream is a caller-owned device buffer of at
+ * least 16 * n16 bytes, 16-byte aligned; src and dst are host arrays of
+ * nsrc / ndst device pointers.  grid: 1 .. 65536 work-groups of 256 threads.
+ * Returns RN_OK, RN_ERR_NULL, RN_ERR_SHAPE, RN_ERR_ALIGN or RN_ERR_LAUNCH;
+ * asynchronous on `stream`.
+ */
+int rn_stream_mix(const void* const* src, int nsrc, void* const* dst, int ndst, int64_t n16, int grid,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,11 @@ HEADER = os.path.join(ROOT, "include", "rmsnorm_gfx950.h")
 def rn():
     lib_path = os.path.join(ROOT, "bwd_fp8_block_amd", "librmsnorm_gfx950.so")
     if not os.path.exists(lib_path):
-        from bwd_fp8_block_amd import build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "bwd_fp8_block_amd_build", os.path.join(ROOT, "bwd_fp8_block_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)      # by path: the package __init__ needs the library
         b.build()
     import bwd_fp8_block_amd as m
     return m
@@ -333,3 +337,23 @@ def test_small_t_backward_is_one_strip_on_any_device(rn):
     for T, H, d in ((8, 4096, 1), (128, 256, 0), (300, 2048, 1)):
         g = rn.rn_query_policy(1, T, H, d, d, 256)
         assert g["grid"] > 1 and g["grid"] == rn.rn_query_policy(1, T, H, d, d, 304)["grid"]
+
+
+def test_stream_mix_validation(rn):
+    """The ceiling probe rejects bad arguments before any launch (no pointer is dereferenced;
+    n16 = 0 returns without launching)."""
+    f = rn.lib.rn_stream_mix
+    P = ctypes.c_void_p
+    ok = (P * 5)(*([0x7f0000000000] * 5))
+    bad = (P * 1)(0x7f0000001001)
+    null = (P * 1)(None)
+    assert f(None, 1, ok, 1, 16, 256, None) == 1
+    assert f(ok, 1, null, 1, 16, 256, None) == 1
+    assert f(ok, 1, ok, 3, 16, 256, None) == 2            # mix not provided
+    assert f(ok, 5, ok, 5, 16, 256, None) == 2
+    assert f(ok, 1, ok, 1, 16, 0, None) == 2              # grid
+    assert f(ok, 1, ok, 1, -1, 256, None) == 2
+    assert f(bad, 1, ok, 1, 16, 256, None) == 4
+    assert f(ok, 2, bad, 1, 16, 256, None) == 4
+    for r, w in ((1, 1), (2, 1), (3, 1), (2, 2), (4, 5)):
+        assert f(ok, r, ok, w, 0, 256, None) == 0
