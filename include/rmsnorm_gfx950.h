@@ -285,11 +285,12 @@ int add_rmsnorm_fp8_quant(const void* x, int64_t ldx,
 /*
  * Host-only launch policy query (no HIP call; usable without a GPU).
  * op: 0 = forward (also per-head, with T = tokens * heads and H = head_dim),
- * 1 = backward (plain and residual form), 2 = fused fp8 producer, 3 = forward
- * with a residual stream.
+ * 1 = backward, 2 = fused fp8 producer, 3 = forward with a residual stream,
+ * 4 = backward with a residual stream.
  * Fills out[0..6] = { lanes per row, 16-byte vectors per lane, threads per
  * work-group, work-groups (row chunks), rows per work-group pass, kernel id,
- * flags (bit 0: non-temporal streaming loads/stores) }
+ * flags (bit 0: non-temporal streaming loads/stores, bit 1: interleaved row
+ * walk, bits 4-6: row buffers in the ring, 0 meaning the default two) }
  * for a device with `cu_count` compute units.  Returns an rn_status.
  */
 int rn_query_policy(int op, int64_t T, int64_t H, int x_dtype, int w_dtype,

@@ -108,6 +108,14 @@ def test_policy_shapes_of_the_workloads(rn):
     qk = rn.rn_query_policy(0, 8192 * 32, 128, 1, 1, CU)           # per-head rows of 128 bf16
     assert qk["lpr"] == 8 and qk["nv"] == 2 and qk["grid"] == 2048
     assert rn.rn_query_policy(3, 65536, 4096, 1, 1, CU)["grid"] == 256
+    # streaming backward: 512-thread strips with three row buffers; rows wider than 512 lanes take
+    # one row per group, and their residual form keeps two buffers
+    assert b["wgs"] == 512 and (b["flags"] >> 4) & 7 == 3
+    br = rn.rn_query_policy(4, 8192, 4096, 1, 1, CU)
+    assert {k: br[k] for k in ("lpr", "nv", "wgs", "grid", "flags")} == {k: b[k] for k in ("lpr", "nv", "wgs", "grid", "flags")}
+    w = rn.rn_query_policy(1, 8192, 7168, 1, 1, CU)
+    wr = rn.rn_query_policy(4, 8192, 7168, 1, 1, CU)
+    assert w["wgs"] == 896 and (w["flags"] >> 4) & 7 == 3 and (wr["flags"] >> 4) & 7 == 0 and wr["grid"] == w["grid"]
 
 
 def test_policy_rejects_out_of_range(rn):
