@@ -298,8 +298,8 @@ static hipError_t fp8_go(const Fp8Args& a, const Policy& p, hipStream_t s)
 }
 
 #define RN_FP8_VARIANTS(X) X(16, 1, 256) X(32, 1, 256) X(64, 1, 256) X(64, 2, 256) X(64, 3, 256)        \
-    X(64, 4, 256) X(64, 5, 256) X(64, 6, 256) X(64, 7, 256) X(64, 8, 256) X(64, 5, 512) X(64, 6, 512)  \
-    X(64, 7, 512) X(64, 8, 512)
+    X(64, 4, 256) X(64, 5, 256) X(64, 6, 256) X(64, 7, 256) X(64, 8, 256) X(64, 2, 512) X(64, 3, 512)  \
+    X(64, 4, 512) X(64, 5, 512) X(64, 6, 512) X(64, 7, 512) X(64, 8, 512)
 
 bool fp8_variant_exists(int lprc, int nv, int wgs)
 {

@@ -215,22 +215,31 @@ int policy_bwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 }
 
 // Fused fp8 producer: a 1x128 block is 16 lanes, so groups are 16, 32 or a
-// multiple of 64 lanes.  Measured on MI355X (T = 8192): 2-4 wavefronts per
-// row with at most 4 vectors per lane, two work-groups per CU, interleaved
-// rows: 0.89-0.92 of a same-traffic copy for H = 2048 .. 4096.
+// multiple of 64 lanes.  Rows of 129 .. 896 chunks (H = 1152 .. 7168) take
+// 128-lane groups with up to 7 vectors per lane, four groups to a 512-thread
+// work-group; one such work-group per CU once each CU's share of the tensor is
+// at least 10240 chunks, two below that.  Measured on MI355X against two
+// 256-thread work-groups per CU (lpr 128 up to H = 4096, lpr 256 beyond):
+// T = 32768, H = 4096 202 us vs 221 us; T = 32768, H = 2048 102 vs 111;
+// T = 4096 / 16384, H = 7168 47.6 / 189 vs 50.1 / 204; H = 5120 and 6144
+// 3-9% faster; T = 8192, H = 4096 53.5 us either way; T = 8192, H = 2048
+// (8192 chunks per CU) 26.9 us with two 512-thread groups per CU vs 29.1 with
+// one.  Rows of 1024 chunks keep 256 lanes x 4 in 256-thread groups (the
+// 128-lane form was 3% slower at T = 4096, H = 8192).
 int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
 {
     const int nch = (int)(H / 8);
     if (nch <= 16)        { p->lpr = 16; p->nv = 1; }
     else if (nch <= 32)   { p->lpr = 32; p->nv = 1; }
     else if (nch <= 64)   { p->lpr = 64; p->nv = 1; }
-    else if (nch <= 512)  { p->lpr = 128; p->nv = (int)ceil_div(nch, 128); }
+    else if (nch <= 896)  { p->lpr = 128; p->nv = (int)ceil_div(nch, 128); }
     else if (nch <= 1024) { p->lpr = 256; p->nv = (int)ceil_div(nch, 256); }
     else                  { p->lpr = 64 * (int)ceil_div(nch, 64 * 8); p->nv = (int)ceil_div(nch, p->lpr); }
     if (p->lpr > 512) return RN_ERR_SHAPE;
-    p->wgs = wgs_for(p->lpr, 256);
+    const bool wide_groups = p->lpr == 128 && p->nv >= 2;
+    p->wgs = wide_groups ? 512 : wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
-    const int64_t per_cu = 2;
+    const int64_t per_cu = (wide_groups && T * nch >= 10240 * (int64_t)cu) ? 1 : 2;
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;

@@ -64,6 +64,8 @@ CU = 256
     (0, 8192, 4096, 1, 1), (1, 8192, 4096, 1, 1),
     (1, 58497, 2048, 1, 0), (0, 65536, 5120, 1, 0), (1, 65536, 5120, 1, 0),
     (2, 4096, 7168, 1, 1), (2, 8192, 4096, 1, 1), (2, 3, 1152, 1, 1), (2, 1, 128, 1, 1),
+    (2, 8192, 2048, 1, 1), (2, 32768, 2048, 1, 1), (2, 16384, 5120, 1, 1), (2, 1000, 1024, 1, 1),
+    (2, 5, 1152, 1, 1), (2, 8192, 8192, 1, 1),
     (0, 5, 8, 1, 1), (1, 5, 8, 1, 1), (0, 100, 32768, 1, 1), (1, 9, 16384, 1, 1), (2, 9, 32768, 1, 1),
     (0, 7, 17408, 1, 1), (2, 7, 17408, 1, 1), (0, 7, 9216, 0, 0), (2, 7, 9216, 1, 1), (0, 3, 20480, 1, 0),
     (3, 8192, 4096, 1, 1), (3, 64, 256, 0, 0), (3, 5, 8, 1, 1), (3, 100, 120, 1, 1), (3, 33, 5120, 1, 0),
@@ -85,10 +87,13 @@ def test_policy_invariants(rn, op, T, H, xd, wd):
         assert p["lpr"] % 16 == 0                            # 1x128 block = 16 lanes
     # a compiled variant serves it: the same check the library applies to overrides
     lprc = min(p["lpr"], 64)
-    if op in (0, 2, 3):
+    if op in (0, 3):
         assert (lprc, p["nv"]) in {(4, 4), (8, 1), (8, 2), (8, 4), (16, 1), (16, 2), (16, 4), (32, 1), (32, 2),
                                    (32, 4)} or \
             (lprc == 64 and (p["wgs"] <= 256 and 1 <= p["nv"] <= 8 or p["wgs"] <= 512 and 5 <= p["nv"] <= 8))
+    elif op == 2:
+        assert (lprc, p["nv"]) in {(16, 1), (32, 1)} or \
+            (lprc == 64 and (p["wgs"] <= 256 and 1 <= p["nv"] <= 8 or p["wgs"] <= 512 and 2 <= p["nv"] <= 8))
     else:
         assert (lprc, p["nv"]) in {(16, 1), (32, 1), (64, 1), (64, 2)}
     if op == 1:
@@ -101,7 +106,15 @@ def test_policy_shapes_of_the_workloads(rn):
     b = rn.rn_query_policy(1, 8192, 4096, 1, 1, CU)
     assert b["nv"] == 1 and b["lpr"] == 512 and b["grid"] == 256
     q = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
-    assert q["lpr"] == 256 and q["nv"] == 4 and q["grid"] == 512
+    assert q["lpr"] == 128 and q["nv"] == 7 and q["wgs"] == 512 and q["grid"] == 256
+    # the producer: four 128-lane groups per work-group, one work-group per CU for long runs
+    # and two for short ones; rows of 1024 chunks keep 256-lane groups
+    q2 = rn.rn_query_policy(2, 8192, 4096, 1, 1, CU)
+    assert q2["lpr"] == 128 and q2["nv"] == 4 and q2["wgs"] == 512 and q2["grid"] == CU
+    q3 = rn.rn_query_policy(2, 8192, 2048, 1, 1, CU)
+    assert q3["wgs"] == 512 and q3["grid"] == 2 * CU
+    q4 = rn.rn_query_policy(2, 8192, 8192, 1, 1, CU)
+    assert q4["lpr"] == 256 and q4["nv"] == 4 and q4["wgs"] == 256 and q4["grid"] == 2 * CU
     r = rn.rn_query_policy(3, 8192, 4096, 1, 1, CU)
     assert r["lpr"] == 128 and r["nv"] == 4 and r["grid"] == 512 and r["flags"] & 3 == 3
     assert rn.rn_query_policy(0, 65536, 4096, 1, 1, CU)["grid"] == 512
