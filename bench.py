@@ -41,13 +41,28 @@ T = 1 .. 64): the fp32 T=64 H=256 workload and bf16 rows of H = 2048 / 4096,
 forward and backward, back to back on one stream, and prints one JSON line of
 microseconds per call (not the contract line).
 
+`--configs` instead times every workload configuration (fp32 T=64 H=256;
+bf16 T=8192 H=4096; bf16 rows with an fp32 weight at H=2048, T=58497 with
+outlier rows, both dw modes; the fp8 producer at T=4096 H=7168 and T=8192
+H=4096; bf16 rows with an fp32 weight at T=65536 H=5120), each op next to the
+plain streaming pass with its read:write mix and bytes, and prints one JSON
+line of them; `--only NAME` restricts it to one configuration.
+
+The default run also samples the GPU's shader and memory clocks (sysfs DPM
+tables of the card the device sits on) during an untimed window of steps run
+right after the timed ones, and reports them under "clocks".
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next] [--latency] [--ceiling]
+                       [--configs [--only NAME]]
 """
 import argparse
+import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -261,37 +276,220 @@ CEILING_MIXES = {
 }
 
 
+# Grids of the streaming passes (256-thread groups): a pass with one vector per
+# thread per stream and 2 reads : 1 write is fastest at the largest grid.
+CEILING_GRIDS = (512, 1024, 2048, 4096, 8192, 16384)
+
+
+def mix_ceiling(torch, rn, dev, r, w, nb, K):
+    """(best grid, us per call) of rn_stream_mix with r source and w destination
+    streams of nb bytes each, best of the grid sweep; four buffer sets alternate
+    so that no pass finds its inputs in the Infinity Cache."""
+    sets = [([torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(r)],
+             [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(w)]) for _ in range(4)]
+    for src, _ in sets:
+        for t in src:
+            t.fill_(1)
+    best = None
+    for grid in CEILING_GRIDS:
+        for k in range(8):
+            rn.rn_stream_mix(*sets[k % 4], grid)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(K):
+            rn.rn_stream_mix(*sets[k % 4], grid)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        if best is None or us < best[1]:
+            best = (grid, us)
+    del sets
+    torch.cuda.empty_cache()
+    return best
+
+
 def ceiling(torch, rn, dev, T, H, K):
-    """Per-call time of rn_stream_mix for each mix, best of a grid sweep; four
-    buffer sets alternate so that no pass finds its inputs in the Infinity Cache."""
+    """Per-call time of rn_stream_mix for each mix at T x H, best of a grid sweep."""
     out = {}
     for name, (r, w, bytes_per_elem) in CEILING_MIXES.items():
         nb = T * H * bytes_per_elem
-        sets = [([torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(r)],
-                 [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(w)]) for _ in range(4)]
-        for src, _ in sets:
-            for t in src:
-                t.fill_(1)
-        best = None
-        for grid in (512, 1024, 2048, 4096, 8192):
-            for k in range(8):
-                rn.rn_stream_mix(*sets[k % 4], grid)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for k in range(K):
-                rn.rn_stream_mix(*sets[k % 4], grid)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / K
-            if best is None or us < best[1]:
-                best = (grid, us)
+        grid, us = mix_ceiling(torch, rn, dev, r, w, nb, K)
         total = (r + w) * nb
-        out[name] = {"bytes": total, "best_grid": best[0], "us": round(best[1], 2),
-                     "GB/s": round(total / best[1] / 1e3, 1), "pct_of_peak": round(100 * total / best[1] / 1e3 / HBM_PEAK_GBS, 2)}
+        out[name] = {"bytes": total, "best_grid": grid, "us": round(us, 2),
+                     "GB/s": round(total / us / 1e3, 1), "pct_of_peak": round(100 * total / us / 1e3 / HBM_PEAK_GBS, 2)}
+    return out
+
+
+# The workload configurations timed by --configs: (name, T, H, x dtype, w dtype,
+# x standard deviation, outlier-row fraction, ops).  Inputs are drawn on the GPU
+# with the distributions of the parity workloads: x ~ N(0, std^2) with the
+# outlier rows scaled by 50, dy and residual ~ N(0, 1), w = 1 + 0.1 N(0, 1),
+# rounded to the storage dtype; eps = 1e-6.
+CONFIG_RUNS = [
+    ("f32_T64_H256", 64, 256, "f32", "f32", 1.0, 0.0, ("fwd", "bwd")),
+    ("bf16_T8192_H4096", 8192, 4096, "bf16", "bf16", 1.0, 0.0, ("fwd", "bwd")),
+    ("bf16_T58497_H2048_outliers_f32w", 58497, 2048, "bf16", "f32", 2.0, 0.01, ("fwd", "bwd", "bwd_nondet")),
+    ("fp8_T4096_H7168", 4096, 7168, "bf16", "bf16", 1.0, 0.0, ("fp8",)),
+    ("bf16_T65536_H5120_f32w", 65536, 5120, "bf16", "f32", 1.0, 0.0, ("fwd", "bwd")),
+    ("fp8_T8192_H4096", 8192, 4096, "bf16", "bf16", 1.0, 0.0, ("fp8",)),
+]
+# (reads, writes, bytes per element of one stream) of each op's plain-pass twin
+OP_MIX = {"fwd": (1, 1, None), "bwd": (2, 1, None), "bwd_nondet": (2, 1, None), "fp8": (4, 5, 1)}
+
+
+def config_bytes(op, T, H, sx, sw):
+    if op == "fwd":
+        return 2 * T * H * sx + H * sw + 4 * T
+    if op in ("bwd", "bwd_nondet"):
+        return 3 * T * H * sx + H * sw + 4 * T + 4 * H
+    return 9 * T * H + 2 * H + 4 * (H // 128) * ((T + 3) // 4 * 4)
+
+
+def configs(torch, rn, dev, only=None):
+    """Per-launch time of each op at every workload configuration, with the
+    plain streaming pass of the same read:write mix and bytes beside it."""
+    out = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+    for name, T, H, xdt, wdt, std, ofrac, ops in CONFIG_RUNS:
+        if only and name != only:
+            continue
+        xt = torch.float32 if xdt == "f32" else torch.bfloat16
+        wt = torch.float32 if wdt == "f32" else torch.bfloat16
+        sx, sw = (4 if xdt == "f32" else 2), (4 if wdt == "f32" else 2)
+
+        def randn(*shape, scale=1.0):
+            return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * scale
+
+        sets = []
+        for _ in range(2):
+            st = {"w": (1.0 + 0.1 * randn(H)).to(wt)}
+            x = randn(T, H, scale=std)
+            if ofrac > 0:
+                rows = torch.randperm(T, generator=gen, device=dev)[:int(round(ofrac * T))]
+                x[rows] *= 50.0
+            st["x"] = x.to(xt)
+            del x
+            if "fp8" in ops:
+                st["res"] = randn(T, H).to(xt)
+                st["out"] = torch.empty(T, H, dtype=torch.uint8, device=dev)
+                st["sc"] = torch.empty(H // 128, (T + 3) // 4 * 4, dtype=torch.float32, device=dev)
+                st["n"] = torch.empty(T, H, dtype=xt, device=dev)
+            else:
+                st["y"] = torch.empty(T, H, dtype=xt, device=dev)
+                st["rstd"] = torch.empty(T, dtype=torch.float32, device=dev)
+                st["dy"] = randn(T, H).to(xt)
+                st["dx"] = torch.empty(T, H, dtype=xt, device=dev)
+                st["dw"] = torch.empty(H, dtype=torch.float32, device=dev)
+                st["ws"] = torch.empty(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4 + 1, dtype=torch.float32,
+                                       device=dev)
+                rn.rmsnorm_fwd(st["x"], st["w"], st["y"], st["rstd"], EPS)
+            sets.append(st)
+        res = {"T": T, "H": H, "x_dtype": xdt, "w_dtype": wdt, "ops": {}}
+        for op in ops:
+            plans = []
+            for st in sets:
+                if op == "fwd":
+                    plans.append(rn.plan_rmsnorm_fwd(st["x"], st["w"], st["y"], st["rstd"], EPS))
+                elif op == "fp8":
+                    plans.append(rn.plan_add_rmsnorm_fp8_block_quant(st["x"], st["res"], st["w"], st["out"], st["sc"],
+                                                                    st["n"], EPS))
+                else:
+                    plans.append(rn.plan_rmsnorm_bwd(st["dy"], st["x"], st["w"], st["rstd"], st["dx"], st["dw"],
+                                                     deterministic=(op == "bwd"), workspace=st["ws"]))
+            nbytes = config_bytes(op, T, H, sx, sw)
+            K = max(20, min(400, int(20e-3 / (nbytes / 5e12))))
+            ms = per_launch_ms(torch, [[pl] for pl in plans], K)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            e = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                 "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+            r, w, bpe = OP_MIX[op]
+            if T * H >= 1 << 20:                         # the few-row case is launch-bound: no ceiling
+                nb = T * H * (bpe if bpe else sx)
+                grid, us = mix_ceiling(torch, rn, dev, r, w, nb, max(10, K // 2))
+                e.update({"mix": "%dR%dW" % (r, w), "mix_us": round(us, 2), "mix_grid": grid,
+                          "op_vs_mix": round(us / (ms * 1e3), 3)})
+            res["ops"][op] = e
+            log(name, op, e)
+        out[name] = res
         del sets
         torch.cuda.empty_cache()
     return out
+
+
+def _card_sysfs(torch):
+    """sysfs device directory of the card that holds cuda:0 (matched by PCI slot)."""
+    p = torch.cuda.get_device_properties(0)
+    slot = "%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(d, "uevent")) as f:
+                if "PCI_SLOT_NAME=" + slot in f.read():
+                    return d
+        except OSError:
+            continue
+    return None
+
+
+def _dpm(path):
+    """(current MHz, highest level MHz) from a pp_dpm_* table ('1: 2400Mhz *')."""
+    with open(path) as f:
+        lines = f.read().splitlines()
+    cur, top = None, None
+    for l in lines:
+        if ":" not in l or "hz" not in l.lower():
+            continue
+        mhz = int("".join(ch for ch in l.split(":", 1)[1].lower().split("mhz")[0] if ch.isdigit()))
+        top = mhz if top is None else max(top, mhz)
+        if "*" in l:
+            cur = mhz
+    return cur, top
+
+
+def clock_window(torch, plans, seconds=0.3):
+    """Shader and memory clocks sampled every 5 ms while steps run (untimed)."""
+    d = _card_sysfs(torch)
+    if d is None:
+        return None
+    sclk, mclk = os.path.join(d, "pp_dpm_sclk"), os.path.join(d, "pp_dpm_mclk")
+    try:
+        _, sclk_top = _dpm(sclk)
+        _dpm(mclk)
+    except (OSError, ValueError):
+        return None
+    samples = {"sclk": [], "mclk": []}
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                for k, path in (("sclk", sclk), ("mclk", mclk)):
+                    c, _ = _dpm(path)
+                    if c is not None:
+                        samples[k].append(c)
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            run_step(plans[i % 2])
+            i += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+
+    def stats(v):
+        return {"min": min(v), "median": statistics.median(v), "max": max(v)} if v else None
+
+    return {"source": "pp_dpm_sclk / pp_dpm_mclk of %s" % d, "window_s": round(time.perf_counter() - t0, 3),
+            "steps": i, "samples": len(samples["sclk"]), "sclk_mhz": stats(samples["sclk"]),
+            "mclk_mhz": stats(samples["mclk"]), "sclk_top_level_mhz": sclk_top}
 
 
 def per_launch_ms(torch, calls_per_set, K):
@@ -370,6 +568,10 @@ def main():
     ap.add_argument("--latency", action="store_true", help="time single calls at few rows instead")
     ap.add_argument("--ceiling", action="store_true",
                     help="time plain streaming passes with each op's read:write mix instead (practical ceiling)")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload configuration next to its streaming-pass twin instead")
+    ap.add_argument("--only", default=None, help="with --configs: one configuration by name")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the clock-sampling window")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
@@ -388,6 +590,13 @@ def main():
     if args.ceiling:
         print(json.dumps({"stream_mix_ceiling_T%d_H%d" % (T_ROWS, HIDDEN):
                           ceiling(torch, rn, dev, T_ROWS, HIDDEN, min(args.steps, 40))}), flush=True)
+        return
+    if args.configs:
+        names = [c[0] for c in CONFIG_RUNS]
+        if args.only and args.only not in names:
+            print("--only: one of %s" % ", ".join(names), file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"configs": configs(torch, rn, dev, args.only)}), flush=True)
         return
     T, H = T_ROWS, HIDDEN
     gen = torch.Generator(device=dev)
@@ -435,6 +644,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": counters_for(dom)}
 
+    clocks = None if args.no_clocks else clock_window(torch, plans)
+
     next_ops = None
     if not args.no_next:
         del sets, plans
@@ -464,6 +675,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "next_ops": next_ops,
+        "clocks": clocks,
     }
     print(json.dumps(out), flush=True)
 
