@@ -130,9 +130,16 @@ int policy_fwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     else if (nch <= 1024) { p->lpr = 128; p->nv = (int)ceil_div(nch, 128); }
     else                  { p->lpr = 64 * (int)ceil_div(nch, 64 * 8); p->nv = (int)ceil_div(nch, p->lpr); }
     if (p->lpr > 512) return RN_ERR_SHAPE;
-    p->wgs = wgs_for(p->lpr, 256);
+    // Rows of 5-8 vectors per 128-lane group (H = 4104 .. 8192 bf16): four groups
+    // to a 512-thread work-group, one per CU once each CU's share of the tensor is
+    // at least 13312 chunks, two below that.  Measured on MI355X against two
+    // 256-thread work-groups per CU: T = 65536, H = 5120 / 6144 / 7168 219 / 272 /
+    // 320 us vs 232 / 298 / 363; T = 16384 6-10% faster, T = 8192 1-5%; T = 4096,
+    // H = 5120 / 6144 14.6 / 17.4 us with two per CU (15.5 / 18.2 before).
+    const bool wide = p->lpr == 128 && p->nv >= 5;
+    p->wgs = wide ? 512 : wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
-    const int64_t per_cu = fwd_per_cu(T, cu, *p);
+    const int64_t per_cu = wide ? (T * nch >= 13312 * (int64_t)cu ? 1 : 2) : fwd_per_cu(T, cu, *p);
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;
@@ -151,6 +158,10 @@ int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int st = policy_fwd(T, H, x_dtype, cu, p);
     if (st != RN_OK) return st;
+    if (p->lpr == 128 && p->wgs == 512) {        // keeps two 128-lane groups per work-group
+        p->wgs = 256;
+        p->gpw = 2;
+    }
     const int64_t per_cu = p->lpr < 64 ? std::max(1, fwd_per_cu(T, cu, *p) / 2)
                          : (p->nv <= 4 && T <= 64 * (int64_t)cu) ? 2 : 1;
     int64_t g = ceil_div(T, p->gpw);

@@ -72,7 +72,8 @@ CU = 256
     (3, 17, 7168, 1, 1), (3, 9, 8200, 1, 1), (3, 5, 16384, 1, 1), (3, 3, 16384, 0, 0), (3, 2, 32768, 1, 1),
     (3, 1000, 128, 1, 1), (3, 300, 3072, 1, 1), (3, 7, 17408, 1, 1),
     (0, 1 << 21, 128, 1, 1), (0, 65536, 256, 1, 1), (0, 262144, 512, 1, 1), (0, 65536, 1024, 1, 1),
-    (0, 65536, 64, 0, 0), (0, 9, 32, 0, 0),
+    (0, 65536, 64, 0, 0), (0, 9, 32, 0, 0), (0, 4096, 7168, 1, 1), (0, 8192, 8192, 1, 1), (3, 65536, 7168, 1, 1),
+    (0, 3001, 5120, 1, 0),
 ])
 def test_policy_invariants(rn, op, T, H, xd, wd):
     p = rn.rn_query_policy(op, T, H, xd, wd, CU)
@@ -105,6 +106,14 @@ def test_policy_shapes_of_the_workloads(rn):
     assert f["lpr"] == 128 and f["nv"] == 4 and f["grid"] == 1024 and f["flags"] & 3 == 3
     b = rn.rn_query_policy(1, 8192, 4096, 1, 1, CU)
     assert b["nv"] == 1 and b["lpr"] == 512 and b["grid"] == 256
+    # forward rows of 5-8 vectors per 128-lane group: 512-thread work-groups, one per CU on long
+    # runs; the residual form keeps 256-thread groups
+    f5 = rn.rn_query_policy(0, 65536, 5120, 1, 0, CU)
+    assert f5["lpr"] == 128 and f5["nv"] == 5 and f5["wgs"] == 512 and f5["grid"] == CU
+    assert rn.rn_query_policy(0, 4096, 5120, 1, 1, CU)["grid"] == 2 * CU
+    assert rn.rn_query_policy(0, 4096, 7168, 1, 1, CU)["grid"] == CU
+    r5 = rn.rn_query_policy(3, 65536, 5120, 1, 0, CU)
+    assert r5["wgs"] == 256 and r5["gpw"] == 2 and r5["grid"] == CU
     q = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
     assert q["lpr"] == 128 and q["nv"] == 7 and q["wgs"] == 512 and q["grid"] == 256
     # the producer: four 128-lane groups per work-group, one work-group per CU for long runs

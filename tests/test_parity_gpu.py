@@ -104,6 +104,9 @@ FWD_CASES = [
     (129, 2048, "bf16", "f32", 0), (257, 4096, "bf16", "bf16", 4096), (33, 5120, "bf16", "f32", 0),
     (17, 7168, "bf16", "bf16", 0), (9, 8200, "bf16", "bf16", 0), (5, 12288, "bf16", "bf16", 0),
     (3, 32768, "bf16", "bf16", 0), (3, 16384, "f32", "f32", 0), (1000, 128, "bf16", "bf16", 0),
+    # four 128-lane groups per 512-thread work-group: one per CU (long run, ragged last window) and
+    # two per CU (short run, padded rows)
+    (4099, 7168, "bf16", "bf16", 0), (3001, 5120, "bf16", "f32", 64), (2051, 8192, "bf16", "bf16", 0),
 ]
 
 
