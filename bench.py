@@ -72,10 +72,15 @@ METRIC = "RMSNorm fwd+bwd & add-RMSNorm-FP8: achieved HBM GB/s, % of peak"
 HBM_PEAK_GBS = 8000.0
 T_ROWS, HIDDEN, EPS = 8192, 4096, 1e-6
 COUNTERS = os.path.join(ROOT, "profiles", "counters_T8192_H4096.json")
+# Sources whose change invalidates a kernel's recorded traffic: the kernel and
+# its device helpers, and the host file that holds its launch policy.
 KERNEL_SOURCES = {
-    "fwd": ["bwd_fp8_block_amd/csrc/rn_fwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
-    "bwd": ["bwd_fp8_block_amd/csrc/rn_bwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
-    "fp8": ["bwd_fp8_block_amd/csrc/rn_fp8.hip", "bwd_fp8_block_amd/csrc/rn_device.h"],
+    "fwd": ["bwd_fp8_block_amd/csrc/rn_fwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h",
+            "bwd_fp8_block_amd/csrc/rn_host.hip"],
+    "bwd": ["bwd_fp8_block_amd/csrc/rn_bwd.hip", "bwd_fp8_block_amd/csrc/rn_device.h",
+            "bwd_fp8_block_amd/csrc/rn_host.hip"],
+    "fp8": ["bwd_fp8_block_amd/csrc/rn_fp8.hip", "bwd_fp8_block_amd/csrc/rn_device.h",
+            "bwd_fp8_block_amd/csrc/rn_host.hip"],
 }
 KERNEL_NAMES = {"fwd": "k_rmsnorm_fwd", "bwd": "k_rmsnorm_bwd + k_dw_reduce", "fp8": "k_add_rmsnorm_fp8",
                 "fwd_residual": "k_rmsnorm_fwd (residual form)",

@@ -230,13 +230,15 @@ int policy_bwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 // 128-lane groups with up to 7 vectors per lane, four groups to a 512-thread
 // work-group; one such work-group per CU once each CU's share of the tensor is
 // at least 10240 chunks, two below that.  Measured on MI355X against two
-// 256-thread work-groups per CU (lpr 128 up to H = 4096, lpr 256 beyond):
-// T = 32768, H = 4096 202 us vs 221 us; T = 32768, H = 2048 102 vs 111;
-// T = 4096 / 16384, H = 7168 47.6 / 189 vs 50.1 / 204; H = 5120 and 6144
-// 3-9% faster; T = 8192, H = 4096 53.5 us either way; T = 8192, H = 2048
-// (8192 chunks per CU) 26.9 us with two 512-thread groups per CU vs 29.1 with
-// one.  Rows of 1024 chunks keep 256 lanes x 4 in 256-thread groups (the
-// 128-lane form was 3% slower at T = 4096, H = 8192).
+// 256-thread work-groups per CU (lpr 128 up to H = 4096, lpr 256 beyond), for
+// the block-scale, per-tensor and fp16/e5m2 forms: T = 32768, H = 4096 203 /
+// 209 / 199 us vs 221 / 219 / 225; T = 32768, H = 2048 102 vs 111 (block);
+// T = 4096, H = 7168 47.6 / 52.2 / 49.2 vs 50.4 / 52.1 / 51.3; T = 8192,
+// H = 2048 / 3072 2-8% faster; H = 5120 and 6144 3-9% faster.  Rows of 4
+// vectors switch only from 32768 chunks per CU: at T = 8192, H = 4096 the
+// block-scale form ties (53.4 vs 53.2 us) and the per-tensor form is slower
+// (57.5 vs 54.6).  Rows of 1024 chunks keep 256 lanes x 4 in 256-thread
+// groups (the 128-lane form was 3% slower at T = 4096, H = 8192).
 int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
 {
     const int nch = (int)(H / 8);
@@ -247,7 +249,7 @@ int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
     else if (nch <= 1024) { p->lpr = 256; p->nv = (int)ceil_div(nch, 256); }
     else                  { p->lpr = 64 * (int)ceil_div(nch, 64 * 8); p->nv = (int)ceil_div(nch, p->lpr); }
     if (p->lpr > 512) return RN_ERR_SHAPE;
-    const bool wide_groups = p->lpr == 128 && p->nv >= 2;
+    const bool wide_groups = p->lpr == 128 && p->nv >= 2 && (p->nv != 4 || T * nch >= 32768 * (int64_t)cu);
     p->wgs = wide_groups ? 512 : wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
     const int64_t per_cu = (wide_groups && T * nch >= 10240 * (int64_t)cu) ? 1 : 2;
