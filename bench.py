@@ -5,9 +5,10 @@ activations, T = 8192 rows of H = 4096:
     rmsnorm_fwd                   (x -> y, rstd)
     rmsnorm_bwd, deterministic    (dy, x, rstd -> dx, dw)
     add_rmsnorm_fp8_block_quant   (x, residual -> residual, normed, e4m3, scales)
-Each op reads its own buffers, and two buffer sets alternate between steps
-(1.3 GB in flight), so no op finds its inputs in the 256 MB Infinity Cache
-left by the op before it; inputs are resident in HBM when timing starts.
+Each op reads its own buffers, and four buffer sets rotate between steps
+(2.6 GB in flight; every op alone cycles through at least 0.5 GB), so no call
+finds its inputs or its outputs' lines in the 256 MB Infinity Cache left by an
+earlier call; inputs are resident in HBM when timing starts.
 
 After the timed steps, the training pair with a residual stream is timed the
 same way at the same shape and reported under "next_ops" (not part of value):
@@ -100,6 +101,8 @@ def algorithmic_bytes(T, H):
 
 
 QK_HEADS, QK_DIM = 32, 128
+# Buffer sets rotated by the step and per-op timings (see the module docstring).
+NSETS = 4
 
 
 def next_bytes(T, H):
@@ -208,8 +211,9 @@ def make_res_set(torch, gen, dev, T, H, rn):
 
 
 def time_next(torch, rn, gen, dev, T, H, K, W):
-    """Per-launch times of the residual training pair and the QK-norm (two alternating buffer sets)."""
-    sets = [make_res_set(torch, gen, dev, T, H, rn) for _ in range(2)]
+    """Per-launch times of the residual training pair, the QK-norm and the producer variants
+    (rotating buffer sets)."""
+    sets = [make_res_set(torch, gen, dev, T, H, rn) for _ in range(NSETS)]
     nh, D = QK_HEADS, QK_DIM
 
     def band(s, k):
@@ -353,7 +357,8 @@ def config_bytes(op, T, H, sx, sw):
 
 def configs(torch, rn, dev, only=None):
     """Per-launch time of each op at every workload configuration, with the
-    plain streaming pass of the same read:write mix and bytes beside it."""
+    plain streaming pass of the same read:write mix and bytes beside it.  Four
+    buffer sets rotate when a set is below 512 MB, two above."""
     out = {}
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261203)
@@ -368,7 +373,8 @@ def configs(torch, rn, dev, only=None):
             return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * scale
 
         sets = []
-        for _ in range(2):
+        set_bytes = 4 * T * H * sx                       # x, y, dy, dx or x, residual, normed, codes
+        for _ in range(NSETS if set_bytes < (512 << 20) else 2):
             st = {"w": (1.0 + 0.1 * randn(H)).to(wt)}
             x = randn(T, H, scale=std)
             if ofrac > 0:
@@ -483,7 +489,7 @@ def clock_window(torch, plans, seconds=0.3):
     i = 0
     while time.perf_counter() - t0 < seconds:
         for _ in range(50):
-            run_step(plans[i % 2])
+            run_step(plans[i % len(plans)])
             i += 1
         torch.cuda.synchronize()
     stop.set()
@@ -563,6 +569,7 @@ def counters_for(op):
 
 
 def main():
+    global NSETS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -577,6 +584,7 @@ def main():
                     help="time every workload configuration next to its streaming-pass twin instead")
     ap.add_argument("--only", default=None, help="with --configs: one configuration by name")
     ap.add_argument("--no-clocks", action="store_true", help="skip the clock-sampling window")
+    ap.add_argument("--sets", type=int, default=NSETS, help="buffer sets rotated by the timings")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
     args = ap.parse_args()
@@ -603,10 +611,11 @@ def main():
             sys.exit(2)
         print(json.dumps({"configs": configs(torch, rn, dev, args.only)}), flush=True)
         return
+    NSETS = max(2, args.sets)
     T, H = T_ROWS, HIDDEN
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261202)
-    sets = [make_set(torch, gen, dev, T, H, rn) for _ in range(2)]
+    sets = [make_set(torch, gen, dev, T, H, rn) for _ in range(NSETS)]
     plans = [plan_step(rn, s) for s in sets]
     torch.cuda.synchronize()
 
@@ -619,14 +628,14 @@ def main():
         del a, b
 
     for i in range(args.warmup):
-        run_step(plans[i % 2])
+        run_step(plans[i % NSETS])
     torch.cuda.synchronize()
 
     K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        run_step(plans[i % 2])
+        run_step(plans[i % NSETS])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K

@@ -157,6 +157,8 @@ BWD_CASES = [
     (129, 2048, "bf16", "f32", 0), (257, 4096, "bf16", "bf16", 0), (300, 5120, "bf16", "f32", 16),
     (31, 7168, "bf16", "bf16", 0), (9, 8200, "bf16", "bf16", 0), (5, 16384, "bf16", "bf16", 0),
     (4, 8192, "f32", "f32", 0), (2000, 256, "bf16", "bf16", 0), (1100, 128, "f32", "f32", 0),
+    # streaming launch over several windows of 256 strips, ragged last window
+    (4099, 4096, "bf16", "bf16", 0), (5003, 5120, "bf16", "f32", 32),
 ]
 
 
