@@ -49,12 +49,17 @@ H=4096; bf16 rows with an fp32 weight at T=65536 H=5120), each op next to the
 plain streaming pass with its read:write mix and bytes, and prints one JSON
 line of them; `--only NAME` restricts it to one configuration.
 
+`--sweep` instead times the forward, the backward (fixed-order dw) and the
+fp8 producer over the grid H in {256, 512, 2048, 4096, 5120, 6144, 7168} x
+T in {256, 1024, 4096, 16231, 65536} (bf16 rows and weight) and prints one
+JSON line of microseconds and GB/s per op and shape.
+
 The default run also samples the GPU's shader and memory clocks (sysfs DPM
 tables of the card the device sits on) during an untimed window of steps run
 right after the timed ones, and reports them under "clocks".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next] [--latency] [--ceiling]
-                       [--configs [--only NAME]]
+                       [--configs [--only NAME]] [--sweep] [--sets N]
 """
 import argparse
 import glob
@@ -429,6 +434,52 @@ def configs(torch, rn, dev, only=None):
     return out
 
 
+SWEEP_H = (256, 512, 2048, 4096, 5120, 6144, 7168)
+SWEEP_T = (256, 1024, 4096, 16231, 65536)
+
+
+def sweep(torch, rn, dev):
+    """Per-launch time of fwd, bwd and the fp8 producer over the H x T grid (bf16)."""
+    bf = torch.bfloat16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261204)
+    out = []
+    for H in SWEEP_H:
+        for T in SWEEP_T:
+            nsets = NSETS if 6 * T * H * 2 < (512 << 20) else 2
+            sets = []
+            for _ in range(nsets):
+                st = {"w": (1.0 + 0.1 * torch.randn(H, generator=gen, device=dev)).to(bf)}
+                for k in ("x", "dy", "res"):
+                    st[k] = torch.randn(T, H, generator=gen, device=dev).to(bf)
+                st["y"], st["dx"], st["n"] = (torch.empty(T, H, dtype=bf, device=dev) for _ in range(3))
+                st["rstd"] = torch.empty(T, dtype=torch.float32, device=dev)
+                st["dw"] = torch.empty(H, dtype=torch.float32, device=dev)
+                st["ws"] = torch.empty(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4 + 1, dtype=torch.float32, device=dev)
+                st["out"] = torch.empty(T, H, dtype=torch.uint8, device=dev)
+                st["sc"] = torch.empty(H // 128, (T + 3) // 4 * 4, dtype=torch.float32, device=dev)
+                rn.rmsnorm_fwd(st["x"], st["w"], st["y"], st["rstd"], EPS)
+                sets.append(st)
+            row = {"H": H, "T": T}
+            plans = {
+                "fwd": [rn.plan_rmsnorm_fwd(st["x"], st["w"], st["y"], st["rstd"], EPS) for st in sets],
+                "bwd": [rn.plan_rmsnorm_bwd(st["dy"], st["x"], st["w"], st["rstd"], st["dx"], st["dw"],
+                                            deterministic=True, workspace=st["ws"]) for st in sets],
+                "fp8": [rn.plan_add_rmsnorm_fp8_block_quant(st["x"], st["res"], st["w"], st["out"], st["sc"], st["n"],
+                                                            EPS) for st in sets],
+            }
+            for op, pl in plans.items():
+                nbytes = config_bytes(op, T, H, 2, 2)
+                K = max(20, min(400, int(20e-3 / (nbytes / 5e12))))
+                ms = per_launch_ms(torch, [[f] for f in pl], K)
+                row[op] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            log("sweep", row)
+            out.append(row)
+            del sets, plans
+            torch.cuda.empty_cache()
+    return out
+
+
 def _card_sysfs(torch):
     """sysfs device directory of the card that holds cuda:0 (matched by PCI slot)."""
     p = torch.cuda.get_device_properties(0)
@@ -583,6 +634,7 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="time every workload configuration next to its streaming-pass twin instead")
     ap.add_argument("--only", default=None, help="with --configs: one configuration by name")
+    ap.add_argument("--sweep", action="store_true", help="time fwd, bwd and fp8 over the H x T grid instead")
     ap.add_argument("--no-clocks", action="store_true", help="skip the clock-sampling window")
     ap.add_argument("--sets", type=int, default=NSETS, help="buffer sets rotated by the timings")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -603,6 +655,9 @@ def main():
     if args.ceiling:
         print(json.dumps({"stream_mix_ceiling_T%d_H%d" % (T_ROWS, HIDDEN):
                           ceiling(torch, rn, dev, T_ROWS, HIDDEN, min(args.steps, 40))}), flush=True)
+        return
+    if args.sweep:
+        print(json.dumps({"sweep_bf16": sweep(torch, rn, dev)}), flush=True)
         return
     if args.configs:
         names = [c[0] for c in CONFIG_RUNS]
