@@ -327,17 +327,19 @@ static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
     const int pd = (p.flags >> 4) & 7;
     // The residual form is compiled with streaming accesses only.
     const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
-    if constexpr (LPRC == 64 && NV == 1) {
-        // the main variant: pipeline depth is a launch choice
+    if constexpr (NV == 1) {
+        // one vector per lane: pipeline depth is a launch choice
         if (pd == 3) {
             if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3, RES>), g, b, 0, s, a);
             else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3, false>), g, b, 0, s, a);
             return hipGetLastError();
         }
-        if (pd == 4) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4, RES>), g, b, 0, s, a);
-            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4, false>), g, b, 0, s, a);
-            return hipGetLastError();
+        if constexpr (LPRC == 64) {
+            if (pd == 4) {
+                if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4, RES>), g, b, 0, s, a);
+                else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4, false>), g, b, 0, s, a);
+                return hipGetLastError();
+            }
         }
     }
     if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2, RES>), g, b, 0, s, a);

@@ -180,11 +180,12 @@ int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 //   vectors): measured on MI355X at 4.3-5.8 us against 6.5-7.3 us for two
 //   launches.  The strip count then depends only on T and H, so the bits of
 //   dw do not depend on the device's CU count.
-//   Streaming: rows of 64 to 512 lanes take 512-thread groups, wider rows one
+//   Streaming: rows of up to 512 lanes take 512-thread groups, wider rows one
 //   row per group, with three row buffers (two rows of loads in flight per
 //   row group).  Measured on MI355X against 1024-thread groups with two
 //   buffers: bf16 T=8192 H=4096 39.5 us vs 41.3 us, H=2048 T=58497 118 us vs
-//   125 us, H=5120 T=65536 353 us vs 403 us.
+//   125 us, H=5120 T=65536 353 us vs 403 us; short rows (16- and 32-lane
+//   groups) at T=65536: H=128 15.7 us vs 18.1, H=256 22.9 vs 24.6.
 int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int nch = (int)(H / elems_per_chunk(x_dtype));
@@ -202,7 +203,7 @@ int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
         p->grid = 1;
         return RN_OK;
     }
-    if (p->lpr >= 64 && p->nv == 1) {
+    if (p->nv == 1) {
         p->wgs = wgs_for(p->lpr, 512);
         p->gpw = p->wgs / p->lpr;
         p->flags |= 3 << 4;                      // three row buffers

@@ -138,6 +138,9 @@ def test_policy_shapes_of_the_workloads(rn):
     assert b["wgs"] == 512 and (b["flags"] >> 4) & 7 == 3
     br = rn.rn_query_policy(4, 8192, 4096, 1, 1, CU)
     assert {k: br[k] for k in ("lpr", "nv", "wgs", "grid", "flags")} == {k: b[k] for k in ("lpr", "nv", "wgs", "grid", "flags")}
+    for H in (128, 256):                                            # short rows: the same streaming form
+        sb = rn.rn_query_policy(1, 65536, H, 1, 1, CU)
+        assert sb["wgs"] == 512 and (sb["flags"] >> 4) & 7 == 3 and sb["grid"] == CU
     w = rn.rn_query_policy(1, 8192, 7168, 1, 1, CU)
     wr = rn.rn_query_policy(4, 8192, 7168, 1, 1, CU)
     assert w["wgs"] == 896 and (w["flags"] >> 4) & 7 == 3 and (wr["flags"] >> 4) & 7 == 0 and wr["grid"] == w["grid"]

@@ -159,6 +159,8 @@ BWD_CASES = [
     (4, 8192, "f32", "f32", 0), (2000, 256, "bf16", "bf16", 0), (1100, 128, "f32", "f32", 0),
     # streaming launch over several windows of 256 strips, ragged last window
     (4099, 4096, "bf16", "bf16", 0), (5003, 5120, "bf16", "f32", 32),
+    # short rows (16- and 32-lane groups) in 512-thread strips with three row buffers
+    (20003, 128, "bf16", "bf16", 0), (9001, 256, "bf16", "f32", 8),
 ]
 
 
