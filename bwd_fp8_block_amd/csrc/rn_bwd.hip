@@ -225,9 +225,9 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 
     // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in
     // flight while the current row is reduced and written.  The streaming
-    // launch (PD = 3) runs the steady form; two buffers (few rows, short rows,
-    // two vectors per lane) keep the guarded form, measured on MI355X the same
-    // or 0.1-0.25 us faster per call at few rows.
+    // launch (PD = 3) runs the steady form; two buffers (few rows, rows wider
+    // than 1024 chunks) keep the guarded form, measured on MI355X the same or
+    // 0.1-0.25 us faster per call at few rows.
     row_pipeline<PD, (PD >= 3), RowBuf>(n_it, load, process);
 
     // Emit this strip's dw partial: the gpw row groups' accumulators are
@@ -327,14 +327,14 @@ static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
     const int pd = (p.flags >> 4) & 7;
     // The residual form is compiled with streaming accesses only.
     const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
-    if constexpr (NV == 1) {
-        // one vector per lane: pipeline depth is a launch choice
+    if constexpr (NV <= 2) {
+        // pipeline depth is a launch choice
         if (pd == 3) {
             if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3, RES>), g, b, 0, s, a);
             else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3, false>), g, b, 0, s, a);
             return hipGetLastError();
         }
-        if constexpr (LPRC == 64) {
+        if constexpr (LPRC == 64 && NV == 1) {
             if (pd == 4) {
                 if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4, RES>), g, b, 0, s, a);
                 else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4, false>), g, b, 0, s, a);

@@ -180,9 +180,14 @@ int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 //   vectors): measured on MI355X at 4.3-5.8 us against 6.5-7.3 us for two
 //   launches.  The strip count then depends only on T and H, so the bits of
 //   dw do not depend on the device's CU count.
-//   Streaming: rows of up to 512 lanes take 512-thread groups, wider rows one
-//   row per group, with three row buffers (two rows of loads in flight per
-//   row group).  Measured on MI355X against 1024-thread groups with two
+//   Streaming: rows of up to 512 chunks take one vector per lane in 512-thread
+//   groups, wider rows (up to 1024 chunks) two vectors per lane in one group
+//   of at most 512 lanes, with three row buffers (two rows of loads in flight
+//   per row group).  Wide rows, measured on MI355X against one vector per lane
+//   in one group of up to 1024 lanes: H = 5120 / 6144 / 7168 / 8192 at
+//   T = 8192 47.9 / 53.3 / 62.1 / 70.4 us vs 48.0 / 58.1 / 67.4 / 75.9, at
+//   T = 4096 28.6 / 31.6 / 35.8 / 38.9 vs 29.2 / 34.6 / 40.2 / 45.9, T = 65536,
+//   H = 5120 (fp32 weight) 319 vs 341; two such groups per strip were 3x slower.  Measured on MI355X against 1024-thread groups with two
 //   buffers: bf16 T=8192 H=4096 39.5 us vs 41.3 us, H=2048 T=58497 118 us vs
 //   125 us, H=5120 T=65536 353 us vs 403 us; short rows (16- and 32-lane
 //   groups) at T=65536: H=128 15.7 us vs 18.1, H=256 22.9 vs 24.6.
@@ -204,6 +209,10 @@ int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
         return RN_OK;
     }
     if (p->nv == 1) {
+        if (nch > 512) {                         // wide rows: two vectors per lane, one group of <= 512 lanes
+            p->lpr = 64 * (int)ceil_div(nch, 128);
+            p->nv = 2;
+        }
         p->wgs = wgs_for(p->lpr, 512);
         p->gpw = p->wgs / p->lpr;
         p->flags |= 3 << 4;                      // three row buffers
@@ -214,10 +223,14 @@ int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     return RN_OK;
 }
 
-// Backward with a residual stream: as the plain backward, except that rows
+// Backward with a residual stream: as the plain backward, except that groups
 // wider than 512 lanes keep two row buffers: the extra g_residual buffer of a
 // third does not fit the registers of a 1024-thread group (measured on MI355X:
-// bf16 T = 8192, H = 7168, 105 us with three buffers against 92 us with two).
+// bf16 T = 8192, H = 7168 with one vector per lane, 105 us with three buffers
+// against 92 us with two).  The wide-row form of the plain backward (two
+// vectors per lane, one group of at most 512 lanes, three buffers) measured
+// T = 8192 / 65536, H = 5120 63.3 / 484 us against 70.6 / 524 with one vector
+// per lane, and H = 7168 within 3% either way (T = 4096 .. 8192).
 int policy_bwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int st = policy_bwd(T, H, x_dtype, cu, p);

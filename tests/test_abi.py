@@ -133,8 +133,9 @@ def test_policy_shapes_of_the_workloads(rn):
     qk = rn.rn_query_policy(0, 8192 * 32, 128, 1, 1, CU)           # per-head rows of 128 bf16
     assert qk["lpr"] == 8 and qk["nv"] == 2 and qk["grid"] == 2048
     assert rn.rn_query_policy(3, 65536, 4096, 1, 1, CU)["grid"] == 256
-    # streaming backward: 512-thread strips with three row buffers; rows wider than 512 lanes take
-    # one row per group, and their residual form keeps two buffers
+    # streaming backward: 512-thread strips with three row buffers; rows of 513 .. 1024 chunks take
+    # two vectors per lane in one group of at most 512 lanes; wider rows two vectors per lane in
+    # groups of more than 512 lanes with two buffers
     assert b["wgs"] == 512 and (b["flags"] >> 4) & 7 == 3
     br = rn.rn_query_policy(4, 8192, 4096, 1, 1, CU)
     assert {k: br[k] for k in ("lpr", "nv", "wgs", "grid", "flags")} == {k: b[k] for k in ("lpr", "nv", "wgs", "grid", "flags")}
@@ -143,7 +144,12 @@ def test_policy_shapes_of_the_workloads(rn):
         assert sb["wgs"] == 512 and (sb["flags"] >> 4) & 7 == 3 and sb["grid"] == CU
     w = rn.rn_query_policy(1, 8192, 7168, 1, 1, CU)
     wr = rn.rn_query_policy(4, 8192, 7168, 1, 1, CU)
-    assert w["wgs"] == 896 and (w["flags"] >> 4) & 7 == 3 and (wr["flags"] >> 4) & 7 == 0 and wr["grid"] == w["grid"]
+    assert w["lpr"] == 448 and w["nv"] == 2 and w["wgs"] == 448 and (w["flags"] >> 4) & 7 == 3
+    assert {k: wr[k] for k in ("lpr", "nv", "wgs", "grid", "flags")} == {k: w[k] for k in ("lpr", "nv", "wgs", "grid", "flags")}
+    c5 = rn.rn_query_policy(1, 65536, 5120, 1, 0, CU)
+    assert c5["lpr"] == 320 and c5["nv"] == 2 and c5["wgs"] == 320 and c5["grid"] == CU
+    x = rn.rn_query_policy(1, 8192, 12288, 1, 1, CU)                # beyond 1024 chunks
+    assert x["nv"] == 2 and x["lpr"] == 768 and (x["flags"] >> 4) & 7 == 0
 
 
 def test_policy_rejects_out_of_range(rn):
