@@ -65,6 +65,8 @@ HEADS_CASES = [
     (1, 1, 64, "bf16", "bf16", 64, 0, 64),
     (3000, 2, 120, "bf16", "bf16", 128, 0, 256),
     (11, 6, 512, "f32", "f32", 512, 0, 3072),
+    (4099, 7, 128, "bf16", "bf16", 128, 0, 7 * 128),                # many rows: token = row / heads
+    (1500, 40, 128, "bf16", "bf16", 136, 64, 40 * 136 + 64),
 ]
 
 
