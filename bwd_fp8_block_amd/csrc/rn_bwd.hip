@@ -348,7 +348,10 @@ static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
 }
 
 // (group class, vectors per lane, largest work-group) triples compiled.
-#define RN_BWD_VARIANTS(X) X(16, 1, 1024) X(32, 1, 1024) X(64, 1, 512) X(64, 1, 1024) X(64, 2, 512) X(64, 2, 1024)
+// The first match serves a launch, so the 512-thread bounds (a 256-register
+// budget per lane) come before the 1024-thread ones (128 registers).
+#define RN_BWD_VARIANTS(X) X(16, 1, 512) X(16, 1, 1024) X(32, 1, 512) X(32, 1, 1024) X(64, 1, 512) X(64, 1, 1024) \
+    X(64, 2, 512) X(64, 2, 1024)
 
 bool bwd_variant_exists(int lprc, int nv, int wgs)
 {
