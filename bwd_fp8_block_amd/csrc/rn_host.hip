@@ -171,26 +171,28 @@ int policy_fwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     return RN_OK;
 }
 
-// Backward: one vector (8 bf16 / 4 fp32 columns) per lane so that the FP64
-// dw accumulators stay in registers; a row spans ceil(H/chunk/64) wavefronts;
-// one work-group (one row strip) per CU.  Rows wider than 1024 vectors take
-// two vectors per lane.
-//   Few rows: 1024-thread groups, and a single strip that writes dw itself
-//   when each row group walks at most two rows (four for rows of at most 64
-//   vectors): measured on MI355X at 4.3-5.8 us against 6.5-7.3 us for two
-//   launches.  The strip count then depends only on T and H, so the bits of
-//   dw do not depend on the device's CU count.
-//   Streaming: rows of up to 512 chunks take one vector per lane in 512-thread
-//   groups, wider rows (up to 1024 chunks) two vectors per lane in one group
-//   of at most 512 lanes, with three row buffers (two rows of loads in flight
-//   per row group).  Wide rows, measured on MI355X against one vector per lane
-//   in one group of up to 1024 lanes: H = 5120 / 6144 / 7168 / 8192 at
-//   T = 8192 47.9 / 53.3 / 62.1 / 70.4 us vs 48.0 / 58.1 / 67.4 / 75.9, at
-//   T = 4096 28.6 / 31.6 / 35.8 / 38.9 vs 29.2 / 34.6 / 40.2 / 45.9, T = 65536,
-//   H = 5120 (fp32 weight) 319 vs 341; two such groups per strip were 3x slower.  Measured on MI355X against 1024-thread groups with two
-//   buffers: bf16 T=8192 H=4096 39.5 us vs 41.3 us, H=2048 T=58497 118 us vs
-//   125 us, H=5120 T=65536 353 us vs 403 us; short rows (16- and 32-lane
-//   groups) at T=65536: H=128 15.7 us vs 18.1, H=256 22.9 vs 24.6.
+// Backward: few vectors per lane so that the FP64 dw accumulators stay in
+// registers; one work-group (one row strip) per CU.
+//   Few rows: one vector per lane (two beyond 1024 chunks) in 1024-thread
+//   groups, and a single strip that writes dw itself when each row group walks
+//   at most two rows (four for rows of at most 64 vectors): measured on MI355X
+//   at 4.3-5.8 us against 6.5-7.3 us for two launches.  The strip count then
+//   depends only on T and H, so the bits of dw do not depend on the device's
+//   CU count.
+//   Streaming: rows of up to 512 chunks take one vector per lane (16- and
+//   32-lane groups for rows of up to 16 / 32 chunks) in 512-thread groups;
+//   rows of 513 .. 1024 chunks two vectors per lane in one group of at most 512
+//   lanes; both with three row buffers (two rows of loads in flight per row
+//   group).  Rows wider than 1024 chunks take two vectors per lane in one group
+//   of more than 512 lanes with two buffers.  Measured on MI355X:
+//   - against 1024-thread groups with two buffers: bf16 T=8192 H=4096 39.5 us
+//     vs 41.3, H=2048 T=58497 118 vs 125, H=5120 T=65536 353 vs 403; short rows
+//     at T=65536: H=128 15.7 vs 18.1, H=256 22.9 vs 24.6;
+//   - wide rows against one vector per lane in one group of up to 1024 lanes:
+//     H = 5120 / 6144 / 7168 / 8192 at T = 8192 47.9 / 53.3 / 62.1 / 70.4 us
+//     vs 48.0 / 58.1 / 67.4 / 75.9, at T = 4096 28.6 / 31.6 / 35.8 / 38.9 vs
+//     29.2 / 34.6 / 40.2 / 45.9, T = 65536, H = 5120 (fp32 weight) 319 vs 341;
+//     two such groups per strip were 3x slower.
 int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int nch = (int)(H / elems_per_chunk(x_dtype));
