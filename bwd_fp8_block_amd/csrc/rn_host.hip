@@ -253,8 +253,12 @@ int policy_bwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 // H = 2048 / 3072 2-8% faster; H = 5120 and 6144 3-9% faster.  Rows of 4
 // vectors switch only from 32768 chunks per CU: at T = 8192, H = 4096 the
 // block-scale form ties (53.4 vs 53.2 us) and the per-tensor form is slower
-// (57.5 vs 54.6).  Rows of 1024 chunks keep 256 lanes x 4 in 256-thread
-// groups (the 128-lane form was 3% slower at T = 4096, H = 8192).
+// (57.5 vs 54.6).  Rows of 897 .. 1024 chunks take 256-lane groups with 4
+// vectors per lane, two to a 512-thread work-group, two such work-groups per
+// CU below 32768 chunks per CU and one from there: H = 8192, T = 16384 / 65536
+// 204 / 823 us against 222 / 926 with one group per 256-thread work-group
+// (two per CU), T = 4096 54.1 against 54.7; 128 lanes x 8 took 871 us at
+// T = 65536.
 int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
 {
     const int nch = (int)(H / 8);
@@ -265,10 +269,21 @@ int policy_fp8(int64_t T, int64_t H, int cu, Policy* p)
     else if (nch <= 1024) { p->lpr = 256; p->nv = (int)ceil_div(nch, 256); }
     else                  { p->lpr = 64 * (int)ceil_div(nch, 64 * 8); p->nv = (int)ceil_div(nch, p->lpr); }
     if (p->lpr > 512) return RN_ERR_SHAPE;
-    const bool wide_groups = p->lpr == 128 && p->nv >= 2 && (p->nv != 4 || T * nch >= 32768 * (int64_t)cu);
+    const int64_t cpc = T * nch / cu;           // chunks of one row tensor per CU
+    bool wide_groups = false;                   // 512-thread work-groups
+    int64_t per_cu = 2;
+    if (p->lpr == 128 && p->nv >= 2 && p->nv != 4) {
+        wide_groups = true;
+        per_cu = cpc >= 10240 ? 1 : 2;
+    } else if (p->lpr == 128 && p->nv == 4) {
+        wide_groups = cpc >= 32768;
+        per_cu = wide_groups ? 1 : 2;
+    } else if (p->lpr == 256 && p->nv == 4) {
+        wide_groups = true;
+        per_cu = cpc >= 32768 ? 1 : 2;
+    }
     p->wgs = wide_groups ? 512 : wgs_for(p->lpr, 256);
     p->gpw = p->wgs / p->lpr;
-    const int64_t per_cu = (wide_groups && T * nch >= 10240 * (int64_t)cu) ? 1 : 2;
     int64_t g = ceil_div(T, p->gpw);
     if (g > (int64_t)cu * per_cu) g = (int64_t)cu * per_cu;
     p->grid = g < 1 ? 1 : g;

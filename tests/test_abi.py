@@ -117,16 +117,18 @@ def test_policy_shapes_of_the_workloads(rn):
     q = rn.rn_query_policy(2, 4096, 7168, 1, 1, CU)
     assert q["lpr"] == 128 and q["nv"] == 7 and q["wgs"] == 512 and q["grid"] == 256
     # the producer: four 128-lane groups per work-group, one work-group per CU for long runs
-    # and two for short ones; rows of 4 vectors switch from 32768 chunks per CU; rows of 1024
-    # chunks keep 256-lane groups
+    # and two for short ones; rows of 4 vectors switch from 32768 chunks per CU, as do rows of
+    # 1024 chunks in 256-lane groups
     q2 = rn.rn_query_policy(2, 8192, 4096, 1, 1, CU)
     assert q2["lpr"] == 128 and q2["nv"] == 4 and q2["wgs"] == 256 and q2["grid"] == 2 * CU
     q5 = rn.rn_query_policy(2, 16384, 4096, 1, 1, CU)
     assert q5["lpr"] == 128 and q5["nv"] == 4 and q5["wgs"] == 512 and q5["grid"] == CU
     q3 = rn.rn_query_policy(2, 8192, 2048, 1, 1, CU)
     assert q3["wgs"] == 512 and q3["grid"] == 2 * CU
-    q4 = rn.rn_query_policy(2, 8192, 8192, 1, 1, CU)
-    assert q4["lpr"] == 256 and q4["nv"] == 4 and q4["wgs"] == 256 and q4["grid"] == 2 * CU
+    q4 = rn.rn_query_policy(2, 8192, 8192, 1, 1, CU)               # rows of 1024 chunks: 256 lanes x 4
+    assert q4["lpr"] == 256 and q4["nv"] == 4 and q4["wgs"] == 512 and q4["grid"] == CU
+    q6 = rn.rn_query_policy(2, 4096, 8192, 1, 1, CU)
+    assert q6["lpr"] == 256 and q6["wgs"] == 512 and q6["grid"] == 2 * CU
     r = rn.rn_query_policy(3, 8192, 4096, 1, 1, CU)
     assert r["lpr"] == 128 and r["nv"] == 4 and r["grid"] == 512 and r["flags"] & 3 == 3
     assert rn.rn_query_policy(0, 65536, 4096, 1, 1, CU)["grid"] == 512

@@ -272,7 +272,9 @@ FP8_CASES = [(1, 128, 0), (3, 256, 16), (5, 384, 0), (64, 1152, 0), (129, 2048, 
              (33, 7168, 0), (6, 8192, 0), (3, 16384, 0), (2, 32768, 0), (300, 1024, 0),
              # four 128-lane groups per 512-thread work-group: one work-group per CU (long runs,
              # ragged last window) and two per CU (short runs)
-             (10243, 2048, 0), (4099, 5120, 64), (2050, 3072, 0), (517, 1152, 0), (16387, 4096, 0)]
+             (10243, 2048, 0), (4099, 5120, 64), (2050, 3072, 0), (517, 1152, 0), (16387, 4096, 0),
+             # 256-lane groups of 4 vectors, two per 512-thread work-group, one work-group per CU
+             (8195, 8192, 0)]
 
 
 @pytest.mark.parametrize("T,H,pad", FP8_CASES)
