@@ -50,7 +50,7 @@ plain streaming pass with its read:write mix and bytes, and prints one JSON
 line of them; `--only NAME` restricts it to one configuration.
 
 `--sweep` instead times the forward, the backward (fixed-order dw) and the
-fp8 producer over the grid H in {256, 512, 2048, 4096, 5120, 6144, 7168} x
+fp8 producer over the grid H in {256, 512, 2048, 4096, 5120, 6144, 7168, 8192} x
 T in {256, 1024, 4096, 16231, 65536} (bf16 rows and weight) and prints one
 JSON line of microseconds and GB/s per op and shape.
 
@@ -434,7 +434,7 @@ def configs(torch, rn, dev, only=None):
     return out
 
 
-SWEEP_H = (256, 512, 2048, 4096, 5120, 6144, 7168)
+SWEEP_H = (256, 512, 2048, 4096, 5120, 6144, 7168, 8192)
 SWEEP_T = (256, 1024, 4096, 16231, 65536)
 
 
