@@ -161,6 +161,8 @@ BWD_CASES = [
     (4099, 4096, "bf16", "bf16", 0), (5003, 5120, "bf16", "f32", 32),
     # short rows (16- and 32-lane groups) in 512-thread strips with three row buffers
     (20003, 128, "bf16", "bf16", 0), (9001, 256, "bf16", "f32", 8),
+    # rows of 513 .. 1024 chunks (two vectors per lane, one group of at most 512 lanes): fp32 rows, bf16 rows
+    (3001, 4096, "f32", "f32", 0), (2999, 3000, "f32", "f32", 4), (4097, 7168, "bf16", "bf16", 0),
 ]
 
 

@@ -139,6 +139,8 @@ RES_BWD_CASES = [
     (65, 1000, "bf16", "bf16", 64), (127, 1024, "f32", "f32", 0), (129, 2048, "bf16", "f32", 0),
     (257, 4096, "bf16", "bf16", 0), (300, 5120, "bf16", "f32", 16), (31, 7168, "bf16", "bf16", 0),
     (5, 16384, "bf16", "bf16", 0), (4, 8192, "f32", "f32", 0), (2000, 256, "bf16", "bf16", 0),
+    # rows of 513 .. 1024 chunks: two vectors per lane, three row buffers, many windows
+    (3001, 7168, "bf16", "bf16", 0), (2003, 4096, "f32", "f32", 8),
 ]
 
 
