@@ -33,9 +33,12 @@ Algorithmic bytes count each tensor once (weight once, not per row):
     bwd  3*T*H*2 + 2*H + 4*T + 4*H
     fp8  9*T*H + 2*H + 4*(H/128)*round_up(T,4)
 
-`--ceiling` instead times plain streaming passes (rn_stream_mix) with each op's
-read:write mix and bytes at T x H, the best of a grid sweep, and prints one
-JSON line of them: the practical ceiling the op figures are compared with.
+`--ceiling` instead times plain streaming passes (the bench-side probe in
+bench_probe/, not part of the RMSNorm library) with each op's read:write mix and
+bytes at T x H, and read-only and write-only passes of each op's byte count, each
+the best over the probe's launch shapes (walk order, vectors in flight, group
+size, grid), and prints one JSON line of them: the practical ceiling the op
+figures are compared with.
 
 `--latency` instead times single calls at few rows (the launch-bound regime,
 T = 1 .. 64): the fp32 T=64 H=256 workload and bf16 rows of H = 2048 / 4096,
@@ -290,48 +293,71 @@ CEILING_MIXES = {
 }
 
 
-# Grids of the streaming passes (256-thread groups): a pass with one vector per
-# thread per stream and 2 reads : 1 write is fastest at the largest grid.
-CEILING_GRIDS = (512, 1024, 2048, 4096, 8192, 16384)
+# The streaming passes' launch shapes: every walk order of the probe (grid-stride,
+# the RMSNorm kernels' XCD-aware window, one contiguous chunk per work-group),
+# 1 .. 8 vectors per thread per stream in flight, 256- and 512-thread groups, and
+# grids from one to 64 work-groups per CU (those with at least one tile each).
+CEILING_ORDERS = ("stride", "xcd", "chunk")
+CEILING_VPT = (1, 2, 4, 8)
+CEILING_WGS = (256, 512)
+CEILING_GRIDS = (256, 512, 1024, 2048, 4096, 8192, 16384)
 
 
-def mix_ceiling(torch, rn, dev, r, w, nb, K):
-    """(best grid, us per call) of rn_stream_mix with r source and w destination
-    streams of nb bytes each, best of the grid sweep; four buffer sets alternate
-    so that no pass finds its inputs in the Infinity Cache."""
+def mix_ceiling(torch, probe, dev, r, w, nb, K, shapes=None):
+    """(best launch shape, us per call) of the streaming probe with r source and w
+    destination streams of nb bytes each, best over the launch shapes; four buffer sets
+    alternate so that no pass finds its inputs in the Infinity Cache."""
+    nb = nb // 16 * 16
     sets = [([torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(r)],
              [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(w)]) for _ in range(4)]
     for src, _ in sets:
         for t in src:
             t.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    if shapes is None:
+        shapes = [(o, v, g, grid) for o in CEILING_ORDERS for v in CEILING_VPT for g in CEILING_WGS
+                  for grid in CEILING_GRIDS if grid * g * v <= nb // 16]
     best = None
-    for grid in CEILING_GRIDS:
+    for order, vpt, wgs, grid in shapes:
+        plans = [probe.plan_stream_mix(*st, grid, wgs=wgs, vpt=vpt, order=order, sink=sink) for st in sets]
+
+        def one(k):
+            plans[k % 4]()
         for k in range(8):
-            rn.rn_stream_mix(*sets[k % 4], grid)
+            one(k)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for k in range(K):
-            rn.rn_stream_mix(*sets[k % 4], grid)
+            one(k)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / K
         if best is None or us < best[1]:
-            best = (grid, us)
+            best = ({"order": order, "vpt": vpt, "wgs": wgs, "grid": grid}, us)
     del sets
     torch.cuda.empty_cache()
     return best
 
 
-def ceiling(torch, rn, dev, T, H, K):
-    """Per-call time of rn_stream_mix for each mix at T x H, best of a grid sweep."""
+def ceiling(torch, probe, dev, T, H, K):
+    """Per-call time of the streaming probe for each op's mix at T x H, and of a
+    read-only and a write-only pass of each op's byte count, best over the probe's
+    launch shapes."""
     out = {}
+    runs = []
     for name, (r, w, bytes_per_elem) in CEILING_MIXES.items():
-        nb = T * H * bytes_per_elem
-        grid, us = mix_ceiling(torch, rn, dev, r, w, nb, K)
-        total = (r + w) * nb
-        out[name] = {"bytes": total, "best_grid": grid, "us": round(us, 2),
-                     "GB/s": round(total / us / 1e3, 1), "pct_of_peak": round(100 * total / us / 1e3 / HBM_PEAK_GBS, 2)}
+        runs.append((name, r, w, T * H * bytes_per_elem))
+    for op, total in (("fwd", 2 * T * H * 2), ("bwd", 3 * T * H * 2), ("fp8", 9 * T * H)):
+        nr, nw = min(4, total // (T * H)), min(5, total // (T * H))
+        runs.append(("%s_bytes_read_only_%dR" % (op, nr), nr, 0, total // nr))
+        runs.append(("%s_bytes_write_only_%dW" % (op, nw), 0, nw, total // nw))
+    for name, r, w, nb in runs:
+        shape, us = mix_ceiling(torch, probe, dev, r, w, nb, K)
+        total = (r + w) * (nb // 16 * 16)
+        out[name] = {"bytes": total, "best": shape, "us": round(us, 2), "GB/s": round(total / us / 1e3, 1),
+                     "pct_of_peak": round(100 * total / us / 1e3 / HBM_PEAK_GBS, 2)}
+        log(name, out[name])
     return out
 
 
@@ -360,7 +386,7 @@ def config_bytes(op, T, H, sx, sw):
     return 9 * T * H + 2 * H + 4 * (H // 128) * ((T + 3) // 4 * 4)
 
 
-def configs(torch, rn, dev, only=None):
+def configs(torch, rn, probe, dev, only=None):
     """Per-launch time of each op at every workload configuration, with the
     plain streaming pass of the same read:write mix and bytes beside it.  Four
     buffer sets rotate when a set is below 512 MB, two above."""
@@ -423,8 +449,8 @@ def configs(torch, rn, dev, only=None):
             r, w, bpe = OP_MIX[op]
             if T * H >= 1 << 20:                         # the few-row case is launch-bound: no ceiling
                 nb = T * H * (bpe if bpe else sx)
-                grid, us = mix_ceiling(torch, rn, dev, r, w, nb, max(10, K // 2))
-                e.update({"mix": "%dR%dW" % (r, w), "mix_us": round(us, 2), "mix_grid": grid,
+                shape, us = mix_ceiling(torch, probe, dev, r, w, nb, max(10, K // 2))
+                e.update({"mix": "%dR%dW" % (r, w), "mix_us": round(us, 2), "mix_shape": shape,
                           "op_vs_mix": round(us / (ms * 1e3), 3)})
             res["ops"][op] = e
             log(name, op, e)
@@ -579,30 +605,71 @@ def run_step(calls):
     fp8()
 
 
-def cpu_baseline(T, H):
-    """The CPU oracle on one full step's worth of rows (single thread), in GB/s of
-    the same algorithmic bytes."""
+def host_threads():
+    """Threads for the CPU baseline: the cores this process may run on."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def cpu_step(oracle, d, T, H, nthreads):
+    """One step of the path on the CPU oracle: forward, backward (at the forward's rstd
+    rounded to fp32, as the GPU path stores it) and the fused fp8 producer, over
+    contiguous row chunks run in `nthreads` threads (the oracle is plain sequential C
+    and releases the GIL in each call).  Rows are independent, so every row output is
+    the sequential oracle's; dw is the FP64 sum of the chunks' dw in chunk order.
+    Returns (y, rstd, dx, dw, fp8 dict) with the chunks' rows in place."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
+    n = max(1, min(nthreads, T))
+    bounds = [(T * k // n, T * (k + 1) // n) for k in range(n)]
+    with ThreadPoolExecutor(n) as ex:
+        fw = list(ex.map(lambda b: oracle.rmsnorm_fwd(d["x"][b[0]:b[1]], d["w"], EPS), bounds))
+        r32 = [f[1].astype(np.float32).astype(np.float64) for f in fw]
+        bw = list(ex.map(lambda k: oracle.rmsnorm_bwd(d["dy"][bounds[k][0]:bounds[k][1]],
+                                                      d["x"][bounds[k][0]:bounds[k][1]], d["w"], r32[k]),
+                         range(n)))
+        f8 = list(ex.map(lambda b: oracle.add_rmsnorm_fp8(d["x"][b[0]:b[1]], d["residual"][b[0]:b[1]], d["w"], EPS,
+                                                          scale_ld=max(4, (b[1] - b[0] + 3) // 4 * 4)),
+                         bounds))
+    dw = np.zeros(H, np.float64)
+    for _, dwk in bw:
+        dw += dwk
+    y = np.concatenate([f[0] for f in fw])
+    rstd = np.concatenate([f[1] for f in fw])
+    dx = np.concatenate([b[0] for b in bw])
+    fp8 = {k: np.concatenate([f[k] for f in f8]) for k in ("h", "normed_bf16", "codes")}
+    fp8["scale"] = np.concatenate([f["scale"][:, :b[1] - b[0]] for f, b in zip(f8, bounds)], axis=1)
+    return y, rstd, dx, dw, fp8
+
+
+def cpu_baseline(T, H, min_seconds=10.0):
+    """The CPU oracle on whole steps of the benchmark's shape (T rows of H, bf16), on
+    every core of the process's affinity mask, repeated until at least `min_seconds`
+    have passed; GB/s of the same algorithmic bytes as the GPU figure."""
     import oracle
     from workloads import Workload, generate
     d = generate(Workload("cpu_sample", T, H, "bf16", "bf16", residual=True, seed=9090))
+    n = host_threads()
+    reps = 0
     t0 = time.perf_counter()
-    _, rstd = oracle.rmsnorm_fwd(d["x"], d["w"], EPS)
-    t1 = time.perf_counter()
-    oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float32).astype(np.float64))
-    t2 = time.perf_counter()
-    oracle.add_rmsnorm_fp8(d["x"], d["residual"], d["w"], EPS)
-    t3 = time.perf_counter()
-    b = algorithmic_bytes(T, H)
-    total = sum(b.values())
+    while True:
+        cpu_step(oracle, d, T, H, n)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    total = sum(algorithmic_bytes(T, H).values())
     return {
-        "value": round(total / (t3 - t0) / 1e9, 4),
+        "value": round(reps * total / el / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": n,
         "kind": "oracle",
-        "sample": "one step: fwd + bwd + fused fp8 producer over T=%d rows of H=%d (bf16), single-threaded "
-                  "FP64 C oracle, %.1f s (fwd %.1f s, bwd %.1f s, fp8 %.1f s)" % (T, H, t3 - t0, t1 - t0,
-                                                                                  t2 - t1, t3 - t2),
+        "sample": "%d whole steps (fwd + bwd + fused fp8 producer) over T=%d rows of H=%d (bf16), FP64 C oracle "
+                  "on %d threads over contiguous row chunks (dw combined in chunk order), %.1f s" % (
+                      reps, T, H, n, el),
     }
 
 
@@ -653,8 +720,9 @@ def main():
         print(json.dumps({"latency_us_per_call": latency(torch, rn, dev, args.steps)}), flush=True)
         return
     if args.ceiling:
+        import bench_probe
         print(json.dumps({"stream_mix_ceiling_T%d_H%d" % (T_ROWS, HIDDEN):
-                          ceiling(torch, rn, dev, T_ROWS, HIDDEN, min(args.steps, 40))}), flush=True)
+                          ceiling(torch, bench_probe, dev, T_ROWS, HIDDEN, min(args.steps, 40))}), flush=True)
         return
     if args.sweep:
         print(json.dumps({"sweep_bf16": sweep(torch, rn, dev)}), flush=True)
@@ -664,7 +732,8 @@ def main():
         if args.only and args.only not in names:
             print("--only: one of %s" % ", ".join(names), file=sys.stderr)
             sys.exit(2)
-        print(json.dumps({"configs": configs(torch, rn, dev, args.only)}), flush=True)
+        import bench_probe
+        print(json.dumps({"configs": configs(torch, rn, bench_probe, dev, args.only)}), flush=True)
         return
     NSETS = max(2, args.sets)
     T, H = T_ROWS, HIDDEN

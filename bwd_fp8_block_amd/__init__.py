@@ -27,7 +27,7 @@ __all__ = [
     "rmsnorm_fwd_residual", "rmsnorm_bwd_residual", "plan_rmsnorm_fwd_residual", "plan_rmsnorm_bwd_residual",
     "rmsnorm_fwd_heads", "plan_rmsnorm_fwd_heads", "RN_HEADS_MAX_VECTORS",
     "RN_F16", "RN_E4M3", "RN_E5M2", "add_rmsnorm_fp8_quant", "plan_add_rmsnorm_fp8_quant",
-    "rn_selftest_cvt_e5m2", "rn_selftest_quotient", "rn_stream_mix",
+    "rn_selftest_cvt_e5m2", "rn_selftest_quotient",
 ]
 
 RN_F32 = 0
@@ -80,8 +80,6 @@ lib.rn_selftest_cvt_e5m2.argtypes = [_vp, _vp, _i64, _vp]
 lib.rn_selftest_cvt_e5m2.restype = _i32
 lib.rn_selftest_quotient.argtypes = [_i32, _i32, ctypes.c_uint32, ctypes.c_uint32, _vp, _i64, _vp, _vp, _vp]
 lib.rn_selftest_quotient.restype = _i32
-lib.rn_stream_mix.argtypes = [_vp, _i32, _vp, _i32, _i64, _i32, _vp]
-lib.rn_stream_mix.restype = _i32
 lib.rn_query_policy.argtypes = [_i32, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.rn_query_policy.restype = _i32
 lib.rn_bwd_workspace_bytes_for.argtypes = [_i64, _i64, _i32]
@@ -211,7 +209,7 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
                 workspace: torch.Tensor | None = None) -> None:
     """dx [T,H] and dw [H] (fp32, overwritten) from dy, x, w and the forward's rstd.
     `workspace`: a device tensor of at least rmsnorm_bwd_workspace_bytes(T, H) bytes
-    (required whenever T > 0; its content does not matter)."""
+    (may be None when that size is 0; its content does not matter)."""
     dev, fn, args = _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, workspace)
     with _on(dev):
         st = fn(*args)
@@ -528,19 +526,3 @@ def rn_selftest_quotient(dtype: int, out_format: int, mismatches: torch.Tensor, 
         st = lib.rn_selftest_quotient(dtype, out_format, a_lo, a_hi, ps, ns, mismatches.data_ptr(),
                                       first_bad.data_ptr(), _stream(dev))
     _check("rn_selftest_quotient", st)
-
-
-def rn_stream_mix(src: list, dst: list, grid: int) -> None:
-    """The practical-ceiling probe (see the C header): one streaming pass that reads
-    every tensor of `src` and writes every tensor of `dst`, all of the same byte
-    size (a multiple of 16), contiguous and on one device."""
-    ts = list(src) + list(dst)
-    dev = _dev(tuple(ts))
-    nb = ts[0].numel() * ts[0].element_size()
-    if any(not t.is_contiguous() or t.numel() * t.element_size() != nb for t in ts) or nb % 16:
-        raise ValueError("rn_stream_mix: contiguous tensors of one byte size, a multiple of 16")
-    ps = (ctypes.c_void_p * len(src))(*[t.data_ptr() for t in src])
-    pd = (ctypes.c_void_p * len(dst))(*[t.data_ptr() for t in dst])
-    with _on(dev):
-        st = lib.rn_stream_mix(ps, len(src), pd, len(dst), nb // 16, int(grid), _stream(dev))
-    _check("rn_stream_mix", st)

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librmsnorm_gfx950.so")
-SOURCES = ["rn_host.hip", "rn_fwd.hip", "rn_bwd.hip", "rn_fp8.hip", "rn_probe.hip"]
+SOURCES = ["rn_host.hip", "rn_fwd.hip", "rn_bwd.hip", "rn_fp8.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for every kernel.

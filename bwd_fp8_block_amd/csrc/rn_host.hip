@@ -225,6 +225,17 @@ int policy_bwd(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
     return RN_OK;
 }
 
+// True when the rows of a backward fit one strip's walk: the policy then
+// launches a single work-group that writes dw itself, whatever the CU count,
+// and no workspace is used.  (With any number of CUs the grid of the other
+// case has at least min(3, cu) strips.)
+bool bwd_one_strip(int64_t T, int64_t H, int x_dtype)
+{
+    Policy p{};
+    if (policy_bwd(T, H, x_dtype, 1 << 20, &p) != RN_OK) return false;
+    return p.grid == 1;
+}
+
 // Backward with a residual stream: as the plain backward, except that groups
 // wider than 512 lanes keep two row buffers: the extra g_residual buffer of a
 // third does not fit the registers of a 1024-thread group (measured on MI355X:
@@ -565,8 +576,11 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
             if (overlap(edw, eg)) return RN_ERR_ALIAS;
             if (overlap(edx, eg) && !same_matrix(dx, lddx, gres, ldgr)) return RN_ERR_ALIAS;
         }
-        if (!workspace) return RN_ERR_WORKSPACE;
-        if (!aligned(workspace, 16)) return RN_ERR_ALIGN;
+        // Only a launch of several row strips keeps partial sums in the workspace.
+        if (!bwd_one_strip(T, H, x_dtype)) {
+            if (!workspace) return RN_ERR_WORKSPACE;
+            if (!aligned(workspace, 16)) return RN_ERR_ALIGN;
+        }
     }
 
     int cu = 0;
@@ -580,9 +594,16 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
     }
     if ((st = residual ? policy_bwd_residual(T, H, x_dtype, cu, &p) : policy_bwd(T, H, x_dtype, cu, &p)) != RN_OK)
         return st;
-    const size_t need = workspace_need(p.grid, H);
-    if (workspace_bytes < need) return RN_ERR_WORKSPACE;
-    {
+    // With one row strip its partial is the column sum itself: it goes
+    // straight into dw, with no second launch and no workspace (the same bits
+    // as the reduce of a single partial, which only widens it to FP64 and
+    // back).  A device with a single CU gets one strip for any T; the
+    // workspace was required above all the same.
+    const bool direct = p.grid == 1;
+    if (!direct) {
+        const size_t need = workspace_need(p.grid, H);
+        if (!workspace) return RN_ERR_WORKSPACE;
+        if (workspace_bytes < need) return RN_ERR_WORKSPACE;
         const Extent ews = vec_extent(workspace, (int64_t)(need / 4), 4);
         if (overlap(ews, edy) || overlap(ews, ex) || overlap(ews, ew) || overlap(ews, er) || overlap(ews, edx) ||
             overlap(ews, edw) || (residual && overlap(ews, eg)))
@@ -602,12 +623,9 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
     a.dx = dx; a.lddx = lddx;
     a.T = T; a.H = (int)H; a.nch = (int)(H / elems_per_chunk(x_dtype));
     a.inv_h = 1.0f / (float)H;
-    // Both modes run the same fixed-order reduction (see the header).
+    // Both values of the flag run the same fixed-order reduction and give the
+    // same bits (see the header).
     (void)deterministic;
-    // With one row strip its partial is the column sum itself: it goes
-    // straight into dw, with no second launch (the same bits as the reduce of
-    // a single partial, which only widens it to FP64 and back).
-    const bool direct = p.grid == 1;
     a.part = direct ? dw : static_cast<float*>(workspace);
     a.part_vec = aligned(a.part, 16) ? 1 : 0;
     if (rn::launch_bwd(a, x_dtype, w_dtype, residual ? 1 : 0, p, s) != hipSuccess) return RN_ERR_LAUNCH;
@@ -676,15 +694,19 @@ size_t rn_bwd_workspace_bytes_for(int64_t T, int64_t H, int cu_count)
     if (T == 0) return 0;
     Policy p{};
     // The bf16 and f32 policies give the same strip count bound (<= cu_count);
-    // size for the larger of the two so one workspace serves both.
+    // size for the larger of the two so one workspace serves both.  A launch
+    // of one strip needs none.
     size_t best = 0;
+    bool any = false;
     for (int dt = 0; dt < 2; ++dt) {
         if (H % elems_per_chunk(dt) != 0) continue;
         if (policy_bwd(T, H, dt, cu_count, &p) != RN_OK) continue;
+        any = true;
+        if (bwd_one_strip(T, H, dt)) continue;
         const size_t b = workspace_need(p.grid, H);
         if (b > best) best = b;
     }
-    if (best == 0) return (size_t)-1;
+    if (!any) return (size_t)-1;
     return (best + 255) / 256 * 256;
 }
 

@@ -73,7 +73,7 @@ typedef enum {
     RN_ERR_DTYPE = 3,       /* unknown dtype code or unsupported (x, w) pair     */
     RN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
     RN_ERR_STRIDE = 5,      /* a row stride < H, or not a 16-byte multiple       */
-    RN_ERR_WORKSPACE = 6,   /* deterministic backward: workspace missing/short   */
+    RN_ERR_WORKSPACE = 6,   /* backward: workspace missing or too short          */
     RN_ERR_ALIAS = 7,       /* an output overlaps an input or another output     */
     RN_ERR_DEVICE = 8,      /* no current HIP device, or it is not gfx950        */
     RN_ERR_LAUNCH = 9       /* the kernel launch failed (hipGetLastError)        */
@@ -110,9 +110,13 @@ int rmsnorm_fwd(const void* x, int64_t ldx, int x_dtype,
 
 /*
  * Size in bytes of the workspace that rmsnorm_bwd needs for (T, H) on HIP
- * device `device` (fp32 partial sums: one per row strip and column, H
- * rounded up to a multiple of 16).  The value never decreases with T, so a workspace sized for the
- * largest T can be reused for every smaller T.  Returns 0 for T == 0 and
+ * device `device`  ([C] API and Memory: the caller owns the backward's
+ * workspace, sized by a query on (T, H, device) and reusable across T).
+ * It holds fp32 partial sums, one per row strip and column (H rounded up to
+ * a multiple of 16).  The value never decreases with T, so a workspace sized
+ * for the largest T can be reused for every smaller T.  Returns 0 where no
+ * workspace is used: T == 0, and rows that one strip walks alone (a few rows;
+ * that launch writes dw directly), for bf16 and fp32 rows alike.  Returns
  * (size_t)-1 on invalid arguments or when the device cannot be queried.
  */
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t H, int device);
@@ -128,15 +132,20 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t H, int device);
  * strip's dw partial is accumulated per column in FP64 from exact products
  * and rounded once to fp32 into `workspace`; a second kernel then sums the
  * strip partials of every column in a fixed order in FP64 and rounds once
- * more.  dw is therefore bitwise identical from call to call (the order
- * depends only on T, H and the device's CU count), and every element is
- * within 1e-4 + 1e-4*|ref| of the FP64 sum ([M] Summary).
- *   deterministic: accepted for interface compatibility; both values run the
- *     fixed-order reduction above (adding strip partials with fp32 atomics
- *     was measured over the dw budget at T = 65536, and was not faster).
+ * more.  When the rows fit one strip (a few rows), that strip's partial is
+ * dw itself: one kernel, no workspace.  dw is therefore bitwise identical
+ * from call to call (the order depends only on T, H and the device's CU
+ * count), and every element is within 1e-4 + 1e-4*|ref| of the FP64 sum
+ * ([M] Summary).
+ *   deterministic: both values run the fixed-order reduction above and give
+ *     the same bits.  The non-deterministic form the pages describe (strip
+ *     partials added into dw with fp32 atomics) was measured over the dw
+ *     budget at T = 65536, H = 5120 (1.03x) and no faster, so it is not
+ *     offered; the flag is kept for the interface.
  *   workspace: device memory of at least rmsnorm_bwd_workspace_bytes(T, H,
- *     device) bytes, 16-byte aligned, else RN_ERR_WORKSPACE; its content on
- *     entry does not matter and is garbage on return.
+ *     device) bytes, 16-byte aligned, else RN_ERR_WORKSPACE.  May be NULL
+ *     (with workspace_bytes 0) when that size is 0, whatever the flag.  Its
+ *     content on entry does not matter and is garbage on return.
  *   dy [T, lddy] x_dtype; x [T, ldx] x_dtype; w [H] w_dtype; rstd [T] fp32
  *   dx [T, lddx] x_dtype output; dw [H] fp32 output.
  */
@@ -331,23 +340,6 @@ int rn_selftest_cvt_e5m2(const float* d_in, uint8_t* d_out, int64_t n, void* str
 int rn_selftest_quotient(int dtype, int out_format, uint32_t a_lo, uint32_t a_hi, const float* d_scales,
                          int64_t n_scales, unsigned long long* d_mismatches, uint32_t* d_first_bad,
                          void* stream);
-
-/*
- * Measurement hook, not part of the RMSNorm path: the practical-ceiling
- * probe that the kernels' bandwidth is compared with.  One grid-stride pass
- * over n16 16-byte vectors: vector i of each of the nsrc source streams is
- * read (non-temporal), the reads are combined with XOR and the result is
- * written (non-temporal) to vector i of each of the ndst destination
- * streams, so the pass moves (nsrc + ndst) * 16 * n16 bytes with that
- * read:write mix and no other work.  (nsrc, ndst) is one of (1,1), (2,1),
- * (3,1), (2,2), (4,5).  Every stream is a caller-owned device buffer of at
- * least 16 * n16 bytes, 16-byte aligned; src and dst are host arrays of
- * nsrc / ndst device pointers.  grid: 1 .. 65536 work-groups of 256 threads.
- * Returns RN_OK, RN_ERR_NULL, RN_ERR_SHAPE, RN_ERR_ALIGN or RN_ERR_LAUNCH;
- * asynchronous on `stream`.
- */
-int rn_stream_mix(const void* const* src, int nsrc, void* const* dst, int ndst, int64_t n16, int grid,
-                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -239,9 +239,19 @@ def test_bwd_validation(rn):
     assert call(lddx=100) == 5
     assert call(dx=A + 64) == 7                    # dx overlaps dy
     assert call(dw=A + 64) == 7                    # dw inside dy
-    assert call(ws=None) == 6                      # no workspace
-    assert call(ws=None, det=0) == 6
-    assert call(ws=C + 0x200008) == 4
+    # T = 4 rows of 256 fit one strip: no workspace is used, so none is required (the call then
+    # gets as far as the device query, which fails without a GPU)
+    assert rn.rn_bwd_workspace_bytes_for(4, 256, CU) == 0
+    assert call(ws=None, wsb=0) == 8
+    assert call(ws=None, wsb=0, det=0) == 8
+    assert call(ws=C + 0x200008) == 8              # an unused workspace is not inspected
+    # T = 2048 rows take several strips: the partial sums need the workspace, whatever the flag
+    big = dict(x=A + 0x400000, dx=C, dw=C + 0x400000, T=2048, ws=C + 0x800000)
+    assert rn.rn_bwd_workspace_bytes_for(2048, 256, CU) > 0
+    assert call(**dict(big, ws=None)) == 6
+    assert call(**dict(big, ws=None, det=0)) == 6
+    assert call(**dict(big, ws=C + 0x800008)) == 4
+    assert call(**big) == 8                        # valid arguments: reaches the device query
 
 
 @no_gpu
@@ -381,23 +391,3 @@ def test_small_t_backward_is_one_strip_on_any_device(rn):
     for T, H, d in ((8, 4096, 1), (128, 256, 0), (300, 2048, 1)):
         g = rn.rn_query_policy(1, T, H, d, d, 256)
         assert g["grid"] > 1 and g["grid"] == rn.rn_query_policy(1, T, H, d, d, 304)["grid"]
-
-
-def test_stream_mix_validation(rn):
-    """The ceiling probe rejects bad arguments before any launch (no pointer is dereferenced;
-    n16 = 0 returns without launching)."""
-    f = rn.lib.rn_stream_mix
-    P = ctypes.c_void_p
-    ok = (P * 5)(*([0x7f0000000000] * 5))
-    bad = (P * 1)(0x7f0000001001)
-    null = (P * 1)(None)
-    assert f(None, 1, ok, 1, 16, 256, None) == 1
-    assert f(ok, 1, null, 1, 16, 256, None) == 1
-    assert f(ok, 1, ok, 3, 16, 256, None) == 2            # mix not provided
-    assert f(ok, 5, ok, 5, 16, 256, None) == 2
-    assert f(ok, 1, ok, 1, 16, 0, None) == 2              # grid
-    assert f(ok, 1, ok, 1, -1, 256, None) == 2
-    assert f(bad, 1, ok, 1, 16, 256, None) == 4
-    assert f(ok, 2, bad, 1, 16, 256, None) == 4
-    for r, w in ((1, 1), (2, 1), (3, 1), (2, 2), (4, 5)):
-        assert f(ok, r, ok, w, 0, 256, None) == 0

@@ -58,3 +58,29 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=60)
     assert r.returncode == 2
     assert "single MI355X" in r.stderr
+
+
+def test_cpu_step_on_row_chunks_equals_the_sequential_oracle(oracle):
+    """The CPU baseline's threaded step: every row output has the sequential oracle's bits
+    (rows are independent), dw is within the FP64 summation bound of the sequential sum and
+    the same from run to run."""
+    import numpy as np
+    from workloads import Workload, generate
+    T, H = 203, 512
+    d = generate(Workload("cpu_chunks", T, H, "bf16", "bf16", residual=True, seed=77))
+    y, rstd, dx, dw, f8 = bench.cpu_step(oracle, d, T, H, 5)
+    ys, rs = oracle.rmsnorm_fwd(d["x"], d["w"], bench.EPS)
+    r32 = rs.astype(np.float32).astype(np.float64)
+    dxs, dws = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], r32)
+    f8s = oracle.add_rmsnorm_fp8(d["x"], d["residual"], d["w"], bench.EPS)
+    assert np.array_equal(y, ys) and np.array_equal(rstd, rs) and np.array_equal(dx, dxs)
+    for k in ("h", "normed_bf16", "codes"):
+        assert np.array_equal(f8[k], f8s[k]), k
+    assert np.array_equal(f8["scale"].view(np.uint32), f8s["scale"][:, :T].view(np.uint32))
+    # two FP64 summation orders of the same T terms differ by at most 2 T u sum|term|
+    absum = oracle.rmsnorm_bwd(d["dy"] & np.uint16(0x7FFF), d["x"] & np.uint16(0x7FFF), d["w"], r32,
+                               want_dx=False)[1]
+    assert np.all(np.abs(dw - dws) <= 2 * T * 2.0 ** -53 * absum)
+    _, _, _, dw2, _ = bench.cpu_step(oracle, d, T, H, 5)
+    assert np.array_equal(dw2, dw)
+    assert bench.host_threads() >= 1

@@ -2,15 +2,19 @@
 
 Small and ragged shapes are compared element by element; the five workload
 configurations are run at full size in the launch configuration the benchmark
-times, with sampled rows (and the full dw / rstd / fp8 outputs) checked against
-the oracle.  Every output buffer is surrounded by guard bands that must come
-back untouched."""
+times and compared element by element as well: every row of y and dx (the
+oracle runs on row chunks in parallel threads), and the full dw, rstd and fp8
+outputs.  Edge rows (zero, constant, tiny and huge scales, below eps, one
+extreme element) go through the forward, the backward and the producer.
+Every output buffer is surrounded by guard bands that must come back
+untouched."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_common import (as_f64, assert_guards, check_dw, check_rstd, check_values, guarded_matrix, sample_rows,
-                        to_dev, to_host, torch_dtype)
+from gpu_common import (as_f64, assert_guards, check_dw, check_rstd, check_values, compare_all_rows, edge_inputs,
+                        guarded_matrix, strided_dev, to_dev, to_host, torch_dtype)
+from workloads import to_bf16_bits
 from workloads import CONFIGS, Workload, generate
 
 pytestmark = pytest.mark.gpu
@@ -227,6 +231,104 @@ def test_bwd_det_bitwise_repeatable_with_poisoned_workspace(rn):
         assert np.array_equal(dx, outs[0][0])
 
 
+EDGE_BWD_CASES = [
+    # T, H, x dtype, w dtype, row stride of x, dy and dx (elements), whole-tensor scale of x
+    (128, 4096, "bf16", "bf16", 8192, 1.0),
+    (255, 1024, "f32", "f32", 2048, 1.0),
+    (16172, 4096, "bf16", "bf16", 8192, 1.0),
+    (16231, 2048, "bf16", "f32", 2048, 1.0),
+    (255, 7168, "bf16", "bf16", 7168, 1.0),           # two vectors per lane
+    (16231, 256, "bf16", "bf16", 512, 1.0),           # 32-lane row groups
+    (4099, 4096, "bf16", "bf16", 4096, 1e-3),
+    (4099, 4096, "bf16", "bf16", 4096, 1e3),
+    (255, 1024, "f32", "f32", 1024, 1e-3),
+    (6, 4096, "bf16", "bf16", 8192, 1.0),             # one strip, dw written directly
+]
+
+
+def edge_case(T, H, xd, wd, scale, seed):
+    x, dy, kinds = edge_inputs(T, H, seed, scale)
+    w = (1 + 0.1 * np.random.default_rng(seed + 1).standard_normal(H)).astype(np.float32)
+    cast = to_bf16_bits if xd == "bf16" else (lambda a: a)
+    return cast(x), cast(dy), (to_bf16_bits(w) if wd == "bf16" else w), kinds
+
+
+@pytest.mark.parametrize("T,H,xd,wd,ld,scale", EDGE_BWD_CASES)
+def test_bwd_edge_rows(rn, oracle, T, H, xd, wd, ld, scale):
+    """Forward and backward over the edge rows (zero, constant, x * 1e-3 / 1e3, below eps, one
+    extreme element, dy = 0, dy * 1e3) at the pages' row counts, strided rows and input scales;
+    every row of y and dx and every dw element against the oracle."""
+    x, dy, w, kinds = edge_case(T, H, xd, wd, scale, 2900 + T + H)
+    xdev, dydev, wdev = strided_dev(x, ld), strided_dev(dy, ld), to_dev(w)
+    dt = torch_dtype(x)
+    y = torch.empty(T, H, dtype=dt, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd(xdev, wdev, y, rstd, 1e-6)
+    rh = to_host(rstd)
+    _, rref = oracle.rmsnorm_fwd(x, w, 1e-6, want_y=False)
+    check_rstd(rh, rref)
+    yh = to_host(y)
+    compare_all_rows("y", T, 2048, lambda lo, hi: yh[lo:hi],
+                     lambda lo, hi: oracle.rmsnorm_fwd(x[lo:hi], w, 1e-6)[0], xd == "bf16")
+    dxfull, dx = guarded_matrix(T, H, dt, ld)
+    dwfull, dw = guarded_matrix(1, H, torch.float32)
+    dw = dw.view(H)
+    nbytes = rn.rmsnorm_bwd_workspace_bytes(T, H)
+    ws = torch.full((max(nbytes // 4, 1),), float("nan"), device="cuda") if nbytes else None
+    rn.rmsnorm_bwd(dydev, xdev, wdev, rstd, dx, dw, deterministic=(T % 2 == 0), workspace=ws)
+    torch.cuda.synchronize()
+    assert_guards(dxfull, T, H, ld, name="dx")
+    assert_guards(dwfull, 1, H, H, name="dw")
+    dxh = to_host(dx)
+    r64 = rh.astype(np.float64)
+    compare_all_rows("dx", T, 2048, lambda lo, hi: dxh[lo:hi],
+                     lambda lo, hi: oracle.rmsnorm_bwd(dy[lo:hi], x[lo:hi], w, r64[lo:hi], want_dw=False)[0],
+                     xd == "bf16")
+    _, dwref = oracle.rmsnorm_bwd(dy, x, w, r64, want_dx=False)
+    check_dw(to_host(dw), dwref)
+    for r, k in kinds.items():
+        if k == "zero_dy":
+            assert np.all(as_f64(dxh[r]) == 0.0), "dy = 0 must give dx = 0 (row %d)" % r
+        if k == "zero":
+            assert abs(float(rh[r]) - 1.0 / np.sqrt(np.float32(1e-6))) <= 1e-3, "rstd of a zero row"
+
+
+def one_strip_every_dtype(rn, T, H, cu):
+    """True when the backward of (T, H) runs one strip for every row dtype that takes H."""
+    grids = []
+    for c in (0, 1):
+        try:
+            grids.append(rn.rn_query_policy(1, T, H, c, c, cu)["grid"])
+        except rn.RNError:                       # H out of this dtype's range
+            pass
+    return all(g == 1 for g in grids)
+
+
+@pytest.mark.parametrize("det", [True, False], ids=["det", "nondet"])
+@pytest.mark.parametrize("T,H,xd", [(4, 4096, "bf16"), (64, 256, "f32"), (2, 16384, "bf16")])
+def test_bwd_one_strip_needs_no_workspace(rn, oracle, T, H, xd, det):
+    """Rows that one strip walks (for this row dtype): the call takes NULL for either flag value,
+    and dw has the bits of a call given a (poisoned) workspace.  The size query, which serves
+    both row dtypes, returns 0 only when neither needs one."""
+    d_code = 1 if xd == "bf16" else 0
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert rn.rn_query_policy(1, T, H, d_code, d_code, cu)["grid"] == 1
+    assert (rn.rmsnorm_bwd_workspace_bytes(T, H) == 0) == one_strip_every_dtype(rn, T, H, cu)
+    d = generate(Workload("bwd_nows", T, H, xd, xd, seed=2600 + T + H))
+    _, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6)
+    dyd, xdev, wdev = to_dev(d["dy"]), to_dev(d["x"]), to_dev(d["w"])
+    rd = torch.from_numpy(np.ascontiguousarray(rstd)).cuda()
+    dx = torch.empty_like(xdev)
+    dw = torch.full((H,), float("nan"), device="cuda")
+    rn.rmsnorm_bwd(dyd, xdev, wdev, rd, dx, dw, deterministic=det, workspace=None)
+    dx1, dw1 = to_host(dx), to_host(dw)
+    dxref, dwref = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float64))
+    check_values("dx", dx1, dxref, xd == "bf16")
+    check_dw(dw1, dwref)
+    dx2, dw2 = gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, not det, poison=True)
+    assert np.array_equal(dw2.view(np.uint32), dw1.view(np.uint32)) and np.array_equal(dx2, dx1)
+
+
 # ----------------------------------------------------------------------------
 # fused residual add + RMSNorm + fp8 block quant
 # ----------------------------------------------------------------------------
@@ -323,6 +425,9 @@ def workload(name):
     return _cache[name]
 
 
+CHUNK = 2048          # rows per oracle call when a whole output is compared
+
+
 @pytest.mark.parametrize("name", ["f32_T64_H256", "bf16_T8192_H4096", "bf16_T58497_H2048_outliers_f32w",
                                   "bf16_T65536_H5120_f32w"])
 def test_config_fwd_bwd(rn, oracle, name):
@@ -337,11 +442,11 @@ def test_config_fwd_bwd(rn, oracle, name):
     rstd_h = to_host(rstd)
     _, rref = oracle.rmsnorm_fwd(d["x"], d["w"], wl.eps, want_y=False)
     check_rstd(rstd_h, rref)
-    rows = sample_rows(T)
-    yh = to_host(y[torch.from_numpy(rows).cuda()])
-    yref, _ = oracle.rmsnorm_fwd(np.ascontiguousarray(d["x"][rows]), d["w"], wl.eps)
-    check_values("y", yh, yref, bf)
+    yh = to_host(y)
     del y
+    compare_all_rows("y", T, CHUNK, lambda lo, hi: yh[lo:hi],
+                     lambda lo, hi: oracle.rmsnorm_fwd(d["x"][lo:hi], d["w"], wl.eps)[0], bf)
+    del yh
 
     dx = torch.empty_like(xd)
     dw = torch.empty(H, dtype=torch.float32, device="cuda")
@@ -354,10 +459,12 @@ def test_config_fwd_bwd(rn, oracle, name):
         dws.append(to_host(dw).copy())
         if rep == 0:
             check_dw(dws[0], dwref)
-            dxh = to_host(dx[torch.from_numpy(rows).cuda()])
-            dxref, _ = oracle.rmsnorm_bwd(np.ascontiguousarray(d["dy"][rows]), np.ascontiguousarray(d["x"][rows]),
-                                          d["w"], rstd_h[rows].astype(np.float64), want_dw=False)
-            check_values("dx", dxh, dxref, bf)
+            dxh = to_host(dx)
+            r64 = rstd_h.astype(np.float64)
+            compare_all_rows("dx", T, CHUNK, lambda lo, hi: dxh[lo:hi],
+                             lambda lo, hi: oracle.rmsnorm_bwd(d["dy"][lo:hi], d["x"][lo:hi], d["w"], r64[lo:hi],
+                                                               want_dw=False)[0], bf)
+            del dxh
     for other in dws[1:]:
         assert np.array_equal(other.view(np.uint32), dws[0].view(np.uint32)), "deterministic dw changed"
     rn.rmsnorm_bwd(dyd, xd, wd, rstd, dx, dw, deterministic=False, workspace=ws)
@@ -393,14 +500,20 @@ def test_validation_with_real_buffers(rn):
     assert e.value.status == 7
     torch.cuda.synchronize()
     assert torch.all(y == 3.0) and torch.all(rstd == 5.0)
-    dx = torch.zeros_like(x)
+    # the backward of rows that take several strips needs its workspace, whatever the flag
+    T2 = 2048
+    assert rn.rmsnorm_bwd_workspace_bytes(T2, H) > 0
+    x2 = torch.randn(T2, H, device="cuda").to(torch.bfloat16)
+    r2 = torch.ones(T2, device="cuda")
+    dx = torch.zeros_like(x2)
     dw = torch.full((H,), 9.0, device="cuda")
     small = torch.empty(4, device="cuda")
-    with pytest.raises(rn.RNError) as e:
-        rn.rmsnorm_bwd(x, x, w, rstd, dx, dw, deterministic=True, workspace=small)
-    assert e.value.status == 6
-    with pytest.raises(rn.RNError) as e:
-        rn.rmsnorm_bwd(x, x, w, rstd, dx, dw, deterministic=True, workspace=None)
-    assert e.value.status == 6
+    for det in (True, False):
+        with pytest.raises(rn.RNError) as e:
+            rn.rmsnorm_bwd(x2, x2, w, r2, dx, dw, deterministic=det, workspace=small)
+        assert e.value.status == 6
+        with pytest.raises(rn.RNError) as e:
+            rn.rmsnorm_bwd(x2, x2, w, r2, dx, dw, deterministic=det, workspace=None)
+        assert e.value.status == 6
     torch.cuda.synchronize()
     assert torch.all(dw == 9.0) and torch.all(dx == 0)

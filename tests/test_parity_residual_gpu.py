@@ -4,15 +4,15 @@ rmsnorm_bwd_residual) through the C ABI against the FP64 CPU oracle.
 h_new is compared bit for bit; y, dx_total, rstd and dw to the same
 tolerances as the plain pair.  In-place forms (h_out = x, h_out = u,
 g_residual = dx) must give the same bits as the out-of-place calls.  The
-bf16 T=8192 H=4096 workload is checked at full size in the launch
+bf16 T=8192 H=4096 workload is checked at full size, every row, in the launch
 configuration the benchmark times."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_common import (assert_guards, check_dw, check_rstd, check_values, guarded_matrix, sample_rows, to_dev,
-                        to_host, torch_dtype)
-from workloads import CONFIGS, Workload, generate
+from gpu_common import (as_f64, assert_guards, check_dw, check_rstd, check_values, compare_all_rows, edge_inputs,
+                        guarded_matrix, strided_dev, to_dev, to_host, torch_dtype)
+from workloads import CONFIGS, Workload, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +172,53 @@ def test_bwd_residual_in_place_and_plain_dw(rn, T, H, xd, wd):
     assert np.array_equal(to_host(dwp).view(np.uint32), dw0.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,H,xd,wd,ld,in_place", [
+    (128, 4096, "bf16", "bf16", 8192, False), (255, 1024, "f32", "f32", 2048, True),
+    (16231, 2048, "bf16", "f32", 2048, True), (16172, 7168, "bf16", "bf16", 7168, False),
+    (4, 4096, "bf16", "bf16", 4096, False)])
+def test_bwd_residual_edge_rows(rn, oracle, T, H, xd, wd, ld, in_place):
+    """The residual backward over the edge rows of h_new (zero, constant, x * 1e-3 / 1e3, below
+    eps, one extreme element, dy = 0, dy * 1e3), strided rows, g_residual with its own zero and
+    huge rows, out of place and accumulating in place into dx; every row and dw element."""
+    seed = 5900 + T + H
+    h32, dy32, kinds = edge_inputs(T, H, seed)
+    rng = np.random.default_rng(seed + 2)
+    g32 = rng.standard_normal((T, H), dtype=np.float32)
+    g32[T // 2] = 0.0
+    g32[T - 1] *= np.float32(1e3)
+    w = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    cast = to_bf16_bits if xd == "bf16" else (lambda a: a)
+    h, dy, g = cast(h32), cast(dy32), cast(g32)
+    w = to_bf16_bits(w) if wd == "bf16" else w
+    hdev, dydev, wdev = strided_dev(h, ld), strided_dev(dy, ld), to_dev(w)
+    dt = torch_dtype(h)
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd(hdev, wdev, torch.empty(T, H, dtype=dt, device="cuda"), rstd, 1e-6)
+    rh = to_host(rstd)
+    dxfull, dx = guarded_matrix(T, H, dt, ld)
+    if in_place:
+        dx.copy_(to_dev(g))
+        gdev = dx
+    else:
+        gdev = strided_dev(g, ld)
+    dw = torch.empty(H, dtype=torch.float32, device="cuda")
+    nbytes = rn.rmsnorm_bwd_workspace_bytes(T, H)
+    ws = torch.full((max(nbytes // 4, 1),), float("nan"), device="cuda") if nbytes else None
+    rn.rmsnorm_bwd_residual(dydev, hdev, wdev, rstd, gdev, dx, dw, deterministic=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert_guards(dxfull, T, H, ld, name="dx")
+    dxh = to_host(dx)
+    r64 = rh.astype(np.float64)
+    compare_all_rows("dx_total", T, 2048, lambda lo, hi: dxh[lo:hi],
+                     lambda lo, hi: oracle.rmsnorm_bwd_residual(dy[lo:hi], h[lo:hi], w, r64[lo:hi], g[lo:hi],
+                                                                want_dw=False)[0], xd == "bf16")
+    _, dwref = oracle.rmsnorm_bwd(dy, h, w, r64, want_dx=False)
+    check_dw(to_host(dw), dwref)
+    for r, k in kinds.items():
+        if k == "zero_dy":                          # dx_total is g_residual, exactly
+            assert np.array_equal(as_f64(dxh[r]), as_f64(g[r])), "dy = 0 must give dx_total = g_residual"
+
+
 def test_residual_empty(rn):
     H = 256
     e = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
@@ -217,7 +264,7 @@ def test_residual_validation(rn):
 
 def test_config_residual_pair(rn, oracle):
     """The bf16 T=8192 H=4096 training pair with a residual at full size: h_new in full
-    (bit-exact), rstd and dw in full, y and dx_total on sampled rows; dw repeatable."""
+    (bit-exact), rstd and dw in full, every row of y and dx_total; dw repeatable."""
     wl = CONFIGS["res_bf16_T8192_H4096"]
     d = generate(wl)
     T, H = wl.T, wl.H
@@ -230,10 +277,10 @@ def test_config_residual_pair(rn, oracle):
     assert np.array_equal(hh, oracle.residual_add(d["x"], d["residual"])), "h_new not bit-exact"
     _, rref = oracle.rmsnorm_fwd(hh, d["w"], wl.eps, want_y=False)
     check_rstd(rh, rref)
-    rows = sample_rows(T)
-    yref, _ = oracle.rmsnorm_fwd(np.ascontiguousarray(hh[rows]), d["w"], wl.eps)
-    check_values("y", to_host(y[torch.from_numpy(rows).cuda()]), yref, True)
-    del y, xd, ud
+    yh = to_host(y)
+    compare_all_rows("y", T, 2048, lambda lo, hi: yh[lo:hi],
+                     lambda lo, hi: oracle.rmsnorm_fwd(hh[lo:hi], d["w"], wl.eps)[0], True)
+    del y, yh, xd, ud
 
     dyd, gd = to_dev(d["dy"]), to_dev(d["g_residual"])
     dx = torch.empty_like(h)
@@ -247,7 +294,8 @@ def test_config_residual_pair(rn, oracle):
         dws.append(to_host(dw).copy())
     check_dw(dws[0], dwref)
     assert np.array_equal(dws[1].view(np.uint32), dws[0].view(np.uint32))
-    dxref, _ = oracle.rmsnorm_bwd_residual(np.ascontiguousarray(d["dy"][rows]), np.ascontiguousarray(hh[rows]),
-                                           d["w"], rh[rows].astype(np.float64),
-                                           np.ascontiguousarray(d["g_residual"][rows]), want_dw=False)
-    check_values("dx_total", to_host(dx[torch.from_numpy(rows).cuda()]), dxref, True)
+    dxh = to_host(dx)
+    r64 = rh.astype(np.float64)
+    compare_all_rows("dx_total", T, 2048, lambda lo, hi: dxh[lo:hi],
+                     lambda lo, hi: oracle.rmsnorm_bwd_residual(d["dy"][lo:hi], hh[lo:hi], d["w"], r64[lo:hi],
+                                                                d["g_residual"][lo:hi], want_dw=False)[0], True)
