@@ -27,7 +27,7 @@ __all__ = [
     "rmsnorm_fwd_residual", "rmsnorm_bwd_residual", "plan_rmsnorm_fwd_residual", "plan_rmsnorm_bwd_residual",
     "rmsnorm_fwd_heads", "plan_rmsnorm_fwd_heads", "RN_HEADS_MAX_VECTORS",
     "RN_F16", "RN_E4M3", "RN_E5M2", "add_rmsnorm_fp8_quant", "plan_add_rmsnorm_fp8_quant",
-    "rn_selftest_cvt_e5m2", "rn_selftest_quotient",
+    "rn_selftest_cvt_e5m2", "rn_selftest_quotient", "rmsnorm_bwd_noalloc",
 ]
 
 RN_F32 = 0
@@ -61,6 +61,8 @@ lib.rmsnorm_bwd_workspace_bytes.restype = _sz
 lib.rmsnorm_bwd.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp,
                             _i64, _i64, _i32, _vp, _sz, _vp]
 lib.rmsnorm_bwd.restype = _i32
+lib.rmsnorm_bwd_noalloc.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _i64, _i32, _vp]
+lib.rmsnorm_bwd_noalloc.restype = _i32
 lib.add_rmsnorm_fp8_block_quant.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64,
                                             _i64, _i64, _f32, _vp]
 lib.add_rmsnorm_fp8_block_quant.restype = _i32
@@ -214,6 +216,16 @@ def rmsnorm_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.
     with _on(dev):
         st = fn(*args)
     _check("rmsnorm_bwd", st)
+
+
+def rmsnorm_bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, rstd: torch.Tensor,
+                        dx: torch.Tensor, dw: torch.Tensor, deterministic: bool = True) -> None:
+    """rmsnorm_bwd with the library's own per-device scratch instead of a workspace
+    (nothing is allocated; calls that overlap on one device race on the scratch)."""
+    dev, _, a = _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, None)
+    with _on(dev):
+        st = lib.rmsnorm_bwd_noalloc(*(a[:14] + a[16:]))
+    _check("rmsnorm_bwd_noalloc", st)
 
 
 def _prep_bwd(dy, x, w, rstd, dx, dw, deterministic, workspace):

@@ -15,6 +15,18 @@
 
 using rn::Policy;
 
+// ---------------------------------------------------------------------------
+// Library-owned scratch for rmsnorm_bwd_noalloc: the dw strip partials of a
+// backward launch, for callers that cannot allocate device memory.  Every
+// device that loads the library holds its own copy of this array until the
+// process ends; host code reaches a device's copy only through the address
+// hipGetSymbolAddress returns with that device current (the array's name on
+// the host is a stand-in, not a device address).  256 strips x 8192 columns
+// of fp32: 8 MiB.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchFloats = (size_t)256 * 8192;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -57,6 +69,35 @@ int current_device_cu(int* cu)
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return RN_ERR_DEVICE;
     return device_cu(dev, cu);
+}
+
+// The current device's copy of `scratch`: its address is taken once per
+// device, with that device current, and kept.
+struct ScratchSlot {
+    std::atomic<int> state{0};   // 0 unknown, 1 ok, 2 failed
+    float* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDev];
+
+int current_scratch(float** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return RN_ERR_DEVICE;
+    ScratchSlot& sl = g_scratch[dev];
+    int st = sl.state.load(std::memory_order_acquire);
+    if (st == 0) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        st = sl.state.load(std::memory_order_relaxed);
+        if (st == 0) {
+            void* p = nullptr;
+            st = (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) ? 1 : 2;
+            sl.ptr = static_cast<float*>(p);
+            sl.state.store(st, std::memory_order_release);
+        }
+    }
+    if (st != 1) return RN_ERR_DEVICE;
+    *out = sl.ptr;
+    return RN_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -542,7 +583,8 @@ int check_heads(const void* p, int64_t ld_t, int64_t ld_h, int64_t heads, int64_
 // Backward, plain or with the residual-stream gradient g_residual.
 int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w, int w_dtype,
                const float* rstd, const void* gres, int64_t ldgr, void* dx, int64_t lddx, float* dw, int64_t T,
-               int64_t H, int deterministic, void* workspace, size_t workspace_bytes, void* stream, bool residual)
+               int64_t H, int deterministic, void* workspace, size_t workspace_bytes, void* stream, bool residual,
+               bool use_scratch = false)
 {
     if (!valid_pair(x_dtype, w_dtype)) return RN_ERR_DTYPE;
     int st;
@@ -577,7 +619,7 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
             if (overlap(edx, eg) && !same_matrix(dx, lddx, gres, ldgr)) return RN_ERR_ALIAS;
         }
         // Only a launch of several row strips keeps partial sums in the workspace.
-        if (!bwd_one_strip(T, H, x_dtype)) {
+        if (!use_scratch && !bwd_one_strip(T, H, x_dtype)) {
             if (!workspace) return RN_ERR_WORKSPACE;
             if (!aligned(workspace, 16)) return RN_ERR_ALIGN;
         }
@@ -600,6 +642,14 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
     // back).  A device with a single CU gets one strip for any T; the
     // workspace was required above all the same.
     const bool direct = p.grid == 1;
+    if (!direct && use_scratch) {
+        float* sp = nullptr;
+        if (workspace_need(p.grid, H) > kScratchFloats * sizeof(float)) return RN_ERR_WORKSPACE;
+        if ((st = current_scratch(&sp)) != RN_OK) return st;
+        clear_last_error();
+        workspace = sp;
+        workspace_bytes = kScratchFloats * sizeof(float);
+    }
     if (!direct) {
         const size_t need = workspace_need(p.grid, H);
         if (!workspace) return RN_ERR_WORKSPACE;
@@ -788,6 +838,14 @@ int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_
 {
     return bwd_common(dy, lddy, x, ldx, x_dtype, w, w_dtype, rstd, nullptr, 0, dx, lddx, dw, T, H, deterministic,
                       workspace, workspace_bytes, stream, false);
+}
+
+int rmsnorm_bwd_noalloc(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w,
+                        int w_dtype, const float* rstd, void* dx, int64_t lddx, float* dw, int64_t T, int64_t H,
+                        int deterministic, void* stream)
+{
+    return bwd_common(dy, lddy, x, ldx, x_dtype, w, w_dtype, rstd, nullptr, 0, dx, lddx, dw, T, H, deterministic,
+                      nullptr, 0, stream, false, true);
 }
 
 int rmsnorm_bwd_residual(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_dtype, const void* w,

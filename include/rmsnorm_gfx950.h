@@ -158,6 +158,28 @@ int rmsnorm_bwd(const void* dy, int64_t lddy,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rmsnorm_bwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same operation, arguments, kernels and bits as
+ * rmsnorm_bwd; the strip partials live in a library-owned device array of
+ * 8 MiB, one per device, kept until the process ends.  It holds the partials
+ * of at most 256 row strips of up to 8192 columns: rows that one strip walks
+ * (a few rows) are served at any H, more rows at H <= 8192 on a device of up
+ * to 256 CUs; beyond that the call returns RN_ERR_WORKSPACE and enqueues
+ * nothing.  Calls no allocating routine.  Every call on a device shares that
+ * device's array: calls that overlap in time on one device (different
+ * streams, or host threads without ordering) race on it and may return wrong
+ * dw; calls ordered on one stream do not.  The array's content carries over
+ * from call to call and is never read before it is written.
+ */
+int rmsnorm_bwd_noalloc(const void* dy, int64_t lddy,
+                        const void* x, int64_t ldx, int x_dtype,
+                        const void* w, int w_dtype,
+                        const float* rstd,
+                        void* dx, int64_t lddx, float* dw,
+                        int64_t T, int64_t H, int deterministic, void* stream);
+
+/*
  * Training forward with a residual stream  ([C] API and Design: Forward: the
  * forward that takes a residual returns h_new and normalises it).
  *   h[r,j]  = round_dtype( x[r,j] + u[r,j] )             written to h_out

@@ -391,3 +391,28 @@ def test_small_t_backward_is_one_strip_on_any_device(rn):
     for T, H, d in ((8, 4096, 1), (128, 256, 0), (300, 2048, 1)):
         g = rn.rn_query_policy(1, T, H, d, d, 256)
         assert g["grid"] > 1 and g["grid"] == rn.rn_query_policy(1, T, H, d, d, 304)["grid"]
+
+
+@no_gpu
+def test_bwd_noalloc_validation(rn):
+    """The no-workspace backward runs the same argument checks as rmsnorm_bwd; valid
+    arguments get as far as the device query (which fails without a GPU)."""
+    f = rn.lib.rmsnorm_bwd_noalloc
+    args = dict(dy=A, lddy=256, x=A + 0x400000, ldx=256, xd=1, w=B, wd=1, rstd=B + 0x1000,
+                dx=C, lddx=256, dw=C + 0x400000, T=2048, H=256, det=1)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["dy"], a["lddy"], a["x"], a["ldx"], a["xd"], a["w"], a["wd"], a["rstd"], a["dx"],
+                 a["lddx"], a["dw"], a["T"], a["H"], a["det"], None)
+
+    assert call(xd=0, wd=1) == 3
+    assert call(H=252) == 2
+    assert call(dw=None) == 1
+    assert call(x=A + 0x400008) == 4
+    assert call(lddx=100) == 5
+    assert call(dx=A + 64) == 7
+    assert call() == 8                             # no workspace argument is needed
+    assert call(det=0) == 8
+
