@@ -139,8 +139,14 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     // rstd = 0 (no dot product, no dw contribution) and are not stored.  The
     // loaded registers are not touched until they are used, so the next row's
     // loads stay in flight while the current row is processed.
+    // A row group of 64 lanes or more spans whole wavefronts, so its row is the
+    // same in every lane of a wavefront: row addresses and rstd are then scalar.
+    auto row_of = [&](int it) {
+        const int64_t r = W.row(it);
+        return LPRC == 64 ? wave_uniform(r) : r;
+    };
     auto load = [&](RowBuf& b, int it) {
-        const int64_t rr = W.clamp(W.row(it));
+        const int64_t rr = W.clamp(row_of(it));
         b.rs = a.rstd[rr];
         const u32x4* grow = reinterpret_cast<const u32x4*>(gbase + rr * a.lddy * XB);
         const u32x4* xrow = reinterpret_cast<const u32x4*>(xbase + rr * a.ldx * XB);
@@ -157,13 +163,18 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     };
 
     auto process = [&](const RowBuf& b, int it) {
-        const int64_t r = W.row(it);
+        const int64_t r = row_of(it);
         const bool valid = W.valid(r);
         const float rs = valid ? b.rs : 0.0f;
         // With one vector per lane the unpacked row (g, x, g*w) stays in
         // registers between the two passes; wider lanes unpack it again.
         constexpr bool KEEP = (NV == 1);
         float xk[KEEP ? NV : 1][E], gwk[KEEP ? NV : 1][E];
+        // For bf16 rows the products g*x (exact in fp32) are taken here and
+        // added into the FP64 accumulators after the row's dx is stored, off
+        // the path to the row reduction's barrier; fp32 rows add theirs here.
+        constexpr bool DW_LATE = (XT == DT_BF16);
+        float pgx[DW_LATE ? NV : 1][E];
         // s = sum_j g*w*x (the row's dot product is rstd * s), and the exact
         // dw contributions of this row.
         const double rsd = (double)rs;
@@ -178,8 +189,8 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
             for (int e = 0; e < E; ++e) {
                 const float gw = g[e] * wf[e];
                 sgwx = __builtin_fmaf(gw, x[e], sgwx);
-                if constexpr (XT == DT_BF16)
-                    acc[i][e] = __builtin_fma((double)(g[e] * x[e]), rsd, acc[i][e]);
+                if constexpr (DW_LATE)
+                    pgx[i][e] = g[e] * x[e];
                 else
                     acc[i][e] = __builtin_fma((double)g[e] * (double)x[e], rsd, acc[i][e]);
                 if constexpr (KEEP) {
@@ -221,6 +232,18 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                 if (cok[i]) st16<NT>(dxrow + cix[i], pack<XT>(o));
             }
         }
+        if constexpr (DW_LATE) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[i][e] = __builtin_fma((double)pgx[i][e], rsd, acc[i][e]);
+        }
+        // The row's dw contributions are added now, not deferred past the
+        // next rows (which would keep this row's products live meanwhile).
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) settle(acc[i][e]);
     };
 
     // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in

@@ -59,6 +59,22 @@ __device__ __forceinline__ void st8(u32x2* p, u32x2 v)
 // form across the loop (which would cost registers, not time).
 __device__ __forceinline__ void opaque(u32x4& v) { asm volatile("" : "+v"(v)); }
 
+// Materialise a value in its register at this point of the program: keeps the
+// compiler from sinking the arithmetic that produced it past later work (and
+// holding that work's inputs live in the meantime).
+__device__ __forceinline__ void settle(double& v) { asm volatile("" : "+v"(v)); }
+
+// A value that is the same in every lane of the wavefront, made visible as
+// such to the compiler (it then lives in scalar registers, and addresses built
+// from it use scalar arithmetic).  Only for values that really are uniform: the
+// first active lane's value is taken.
+__device__ __forceinline__ int64_t wave_uniform(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Zero a loaded vector when its chunk or row is out of range (the load itself
 // was issued from a clamped, always valid address).
 __device__ __forceinline__ u32x4 keep_if(bool ok, const u32x4& v)

@@ -370,8 +370,7 @@ void apply_override(int op, int64_t T, int nch, Policy* p)
     if (!ok) return;
     if (o.grid) q.grid = std::max<int64_t>(1, std::min<int64_t>(o.grid, ceil_div(T, q.gpw)));
     else q.grid = std::max<int64_t>(1, std::min<int64_t>(p->grid * p->gpw / q.gpw, ceil_div(T, q.gpw)));
-    if (op == 1 && q.grid > p->grid) q.grid = p->grid;   // workspace is sized for the default
-    *p = q;
+    *p = q;     // for the backward, the caller checks the workspace against the new grid
 }
 
 void log_policy(const char* op, int64_t T, int64_t H, const Policy& p)
@@ -636,6 +635,8 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
     }
     if ((st = residual ? policy_bwd_residual(T, H, x_dtype, cu, &p) : policy_bwd(T, H, x_dtype, cu, &p)) != RN_OK)
         return st;
+    apply_override(1, T, (int)(H / elems_per_chunk(x_dtype)), &p);
+    log_policy(residual ? "bwd_residual" : "bwd", T, H, p);
     // With one row strip its partial is the column sum itself: it goes
     // straight into dw, with no second launch and no workspace (the same bits
     // as the reduce of a single partial, which only widens it to FP64 and
@@ -659,8 +660,6 @@ int bwd_common(const void* dy, int64_t lddy, const void* x, int64_t ldx, int x_d
             overlap(ews, edw) || (residual && overlap(ews, eg)))
             return RN_ERR_ALIAS;
     }
-    apply_override(1, T, (int)(H / elems_per_chunk(x_dtype)), &p);
-    log_policy(residual ? "bwd_residual" : "bwd", T, H, p);
 
     rn::BwdArgs a{};
     a.lpr = p.lpr;
