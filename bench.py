@@ -705,7 +705,8 @@ def main():
     ap.add_argument("--no-clocks", action="store_true", help="skip the clock-sampling window")
     ap.add_argument("--sets", type=int, default=NSETS, help="buffer sets rotated by the timings")
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (for counter calibration under a profiler)")
+                    help="also run a plain 1 GiB device copy and 1 GiB read-only and write-only streaming passes "
+                         "(for counter calibration under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the RMSNorm path on a single MI355X and has "
@@ -744,12 +745,21 @@ def main():
     torch.cuda.synchronize()
 
     if args.calibration_copy:
+        # kernels of known HBM traffic for the counter passes of a profiler: a 1 GiB device
+        # copy (1 GiB read, 1 GiB written) and the streaming probe's read-only and write-only
+        # passes over four 256 MiB streams (1 GiB read; 1 GiB written)
+        import bench_probe
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
+        q = [t.view(-1) for t in a.view(4, -1)]
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            bench_probe.stream_mix(q, [], 1024, wgs=256, vpt=4, order="stride", sink=sink)
+            bench_probe.stream_mix([], [t.view(-1) for t in b.view(4, -1)], 1024, wgs=256, vpt=4, order="stride")
         torch.cuda.synchronize()
-        del a, b
+        del a, b, q
 
     for i in range(args.warmup):
         run_step(plans[i % NSETS])
