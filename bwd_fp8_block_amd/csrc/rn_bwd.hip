@@ -170,10 +170,17 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
         // registers between the two passes; wider lanes unpack it again.
         constexpr bool KEEP = (NV == 1);
         float xk[KEEP ? NV : 1][E], gwk[KEEP ? NV : 1][E];
-        // For bf16 rows the products g*x (exact in fp32) are taken here and
-        // added into the FP64 accumulators after the row's dx is stored, off
-        // the path to the row reduction's barrier; fp32 rows add theirs here.
-        constexpr bool DW_LATE = (XT == DT_BF16);
+        // Rows of two vectors per lane, bf16: the products g*x (exact in
+        // fp32) are taken here and added into the FP64 accumulators after the
+        // row's dx is stored, pinned there (below), off the path to the row
+        // reduction's barrier.  Left to itself the compiler defers the
+        // accumulation of a whole unrolled block of rows past its last store,
+        // which in this form costs spills; with one vector per lane that
+        // deferral fits in registers and measured as fast or faster, so those
+        // forms (and fp32 rows) add their products here and leave the
+        // schedule to the compiler.
+        constexpr bool PIN = (NV > 1);
+        constexpr bool DW_LATE = PIN && (XT == DT_BF16);
         float pgx[DW_LATE ? NV : 1][E];
         // s = sum_j g*w*x (the row's dot product is rstd * s), and the exact
         // dw contributions of this row.
@@ -191,6 +198,8 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
                 sgwx = __builtin_fmaf(gw, x[e], sgwx);
                 if constexpr (DW_LATE)
                     pgx[i][e] = g[e] * x[e];
+                else if constexpr (XT == DT_BF16)
+                    acc[i][e] = __builtin_fma((double)(g[e] * x[e]), rsd, acc[i][e]);
                 else
                     acc[i][e] = __builtin_fma((double)g[e] * (double)x[e], rsd, acc[i][e]);
                 if constexpr (KEEP) {
@@ -238,12 +247,14 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[i][e] = __builtin_fma((double)pgx[i][e], rsd, acc[i][e]);
         }
-        // The row's dw contributions are added now, not deferred past the
-        // next rows (which would keep this row's products live meanwhile).
+        if constexpr (PIN) {
+            // The row's dw contributions are added now, not deferred past the
+            // next rows (which would keep this row's products live meanwhile).
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
+            for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int e = 0; e < E; ++e) settle(acc[i][e]);
+                for (int e = 0; e < E; ++e) settle(acc[i][e]);
+        }
     };
 
     // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in
