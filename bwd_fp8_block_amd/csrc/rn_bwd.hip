@@ -27,9 +27,14 @@
 // Each strip writes its fp32 partial row to the workspace, and a second
 // kernel sums the G partials of every column in a fixed order in FP64 (no
 // atomics: the result depends only on T, H and G, and is bitwise repeatable).
-// Adding the strip partials with fp32 atomics instead was measured over the
-// per-element dw budget at T = 65536, H = 5120 (1.03x), and was not faster
-// than this second kernel, so both modes of the entry point use this path.
+// When one strip walks all the rows (a few rows), its partial is dw itself
+// and is written there directly: one launch, no workspace.  Adding the strip
+// partials with fp32 atomics instead was measured over the per-element dw
+// budget at T = 65536, H = 5120 (1.03x), and was not faster than this second
+// kernel, so both modes of the entry point use this path.  A single launch
+// would need the strips to wait for the last one before the column sums can
+// start (every partial is complete only at the end of its strip), that is a
+// grid-wide barrier; it is not used.
 //
 // Residual form (RES; [C] API and Design: Backward, the training backward
 // with a residual): the gradient arriving along the residual stream is added
