@@ -111,6 +111,8 @@ FWD_CASES = [
     # four 128-lane groups per 512-thread work-group: one per CU (long run, ragged last window) and
     # two per CU (short run, padded rows)
     (4099, 7168, "bf16", "bf16", 0), (3001, 5120, "bf16", "f32", 64), (2051, 8192, "bf16", "bf16", 0),
+    # the narrowest rows: one 16-byte vector (fp32 H = 4, bf16 H = 8)
+    (5, 4, "f32", "f32", 0), (300, 4, "f32", "f32", 4), (9, 8, "bf16", "f32", 0),
 ]
 
 
@@ -167,6 +169,8 @@ BWD_CASES = [
     (20003, 128, "bf16", "bf16", 0), (9001, 256, "bf16", "f32", 8),
     # rows of 513 .. 1024 chunks (two vectors per lane, one group of at most 512 lanes): fp32 rows, bf16 rows
     (3001, 4096, "f32", "f32", 0), (2999, 3000, "f32", "f32", 4), (4097, 7168, "bf16", "bf16", 0),
+    # the narrowest rows: one 16-byte vector (fp32 H = 4, bf16 H = 8), few and many rows
+    (7, 4, "f32", "f32", 0), (5000, 4, "f32", "f32", 4), (3, 8, "bf16", "f32", 0), (4099, 8, "bf16", "bf16", 8),
 ]
 
 

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import assert_guards, check_rstd, check_values, compare_all_rows, guarded_matrix, to_dev, to_host
+from gpu_common import (as_f64, assert_guards, check_rstd, check_values, compare_all_rows, guarded_matrix, to_dev,
+                        to_host)
 from workloads import CONFIGS, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -99,6 +100,30 @@ def test_heads_in_place_on_fused_buffer(rn, oracle, band):
     outside[:, off: off + nh * D] = False
     assert np.array_equal(after[outside], host[outside]), "values outside the band changed"
     assert np.array_equal(after[:, off: off + nh * D].reshape(T, nh, D), y0)
+
+
+def test_heads_edge_rows(rn, oracle):
+    """Heads of zeros (rstd = 1/sqrt(eps), y = 0), constant heads (y = sign * w), heads scaled by
+    1e-3 and 1e3, a head below eps and one extreme element, spread over tokens and head slots."""
+    T, nh, D = 40, 8, 128
+    rng = np.random.default_rng(6400)
+    a = rng.standard_normal((T, nh, D)).astype(np.float32)
+    a[0, 0] = 0.0
+    a[1, 7] = 2.5
+    a[2, 3] = -0.75
+    a[3, 1] *= 1e-3
+    a[T - 1, 5] *= 1e3
+    a[T // 2, 2] *= 1e-20
+    a[T // 2 + 1, 6, 17] = 3e4
+    host = to_bf16_bits(a.reshape(T, nh * D))
+    w = to_bf16_bits((1 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    y, rstd, _ = run_heads(rn, host, nh, D, D, 0, w, 1e-6)
+    yref, rref = oracle.rmsnorm_fwd_heads(host, nh, D, w, 1e-6)
+    check_rstd(rstd.reshape(-1), rref.reshape(-1))
+    check_values("y", y.reshape(T * nh, D), yref.reshape(T * nh, D), True)
+    y3 = y.reshape(T, nh, D)
+    assert np.all((y3[0, 0] & 0x7FFF) == 0)
+    np.testing.assert_allclose(as_f64(y3[1, 7]), as_f64(w), rtol=2 ** -7)
 
 
 def test_heads_without_rstd(rn, oracle):
