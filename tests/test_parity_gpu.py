@@ -113,6 +113,8 @@ FWD_CASES = [
     (4099, 7168, "bf16", "bf16", 0), (3001, 5120, "bf16", "f32", 64), (2051, 8192, "bf16", "bf16", 0),
     # the narrowest rows: one 16-byte vector (fp32 H = 4, bf16 H = 8)
     (5, 4, "f32", "f32", 0), (300, 4, "f32", "f32", 4), (9, 8, "bf16", "f32", 0),
+    # the widest rows (512-lane groups of up to 8 vectors) over many windows, ragged last window
+    (1500, 32768, "bf16", "bf16", 0), (777, 16384, "f32", "f32", 16), (1301, 12288, "bf16", "f32", 0),
 ]
 
 
@@ -171,6 +173,9 @@ BWD_CASES = [
     (3001, 4096, "f32", "f32", 0), (2999, 3000, "f32", "f32", 4), (4097, 7168, "bf16", "bf16", 0),
     # the narrowest rows: one 16-byte vector (fp32 H = 4, bf16 H = 8), few and many rows
     (7, 4, "f32", "f32", 0), (5000, 4, "f32", "f32", 4), (3, 8, "bf16", "f32", 0), (4099, 8, "bf16", "bf16", 8),
+    # rows wider than 1024 chunks (two vectors per lane in groups of up to 1024 lanes, two row buffers) over
+    # many windows: the widest bf16 and fp32 rows, and an fp32 weight
+    (3000, 16384, "bf16", "bf16", 0), (1203, 8192, "f32", "f32", 0), (2101, 12288, "bf16", "f32", 8),
 ]
 
 
@@ -382,7 +387,9 @@ FP8_CASES = [(1, 128, 0), (3, 256, 16), (5, 384, 0), (64, 1152, 0), (129, 2048, 
              # ragged last window) and two per CU (short runs)
              (10243, 2048, 0), (4099, 5120, 64), (2050, 3072, 0), (517, 1152, 0), (16387, 4096, 0),
              # 256-lane groups of 4 vectors, two per 512-thread work-group, one work-group per CU
-             (8195, 8192, 0)]
+             (8195, 8192, 0),
+             # the widest rows over many windows
+             (1500, 32768, 0), (1111, 16384, 32)]
 
 
 @pytest.mark.parametrize("T,H,pad", FP8_CASES)

@@ -89,6 +89,8 @@ RES_FWD_CASES = [
     (33, 5120, "bf16", "f32", 16), (17, 7168, "bf16", "bf16", 0), (9, 8200, "bf16", "bf16", 0),
     (5, 16384, "bf16", "bf16", 0), (3, 16384, "f32", "f32", 0), (2, 32768, "bf16", "bf16", 0),
     (1000, 128, "bf16", "bf16", 0), (300, 3072, "bf16", "bf16", 0),
+    # the widest rows over many windows
+    (1200, 32768, "bf16", "bf16", 0), (700, 16384, "f32", "f32", 0),
 ]
 
 
@@ -141,6 +143,8 @@ RES_BWD_CASES = [
     (5, 16384, "bf16", "bf16", 0), (4, 8192, "f32", "f32", 0), (2000, 256, "bf16", "bf16", 0),
     # rows of 513 .. 1024 chunks: two vectors per lane, three row buffers, many windows
     (3001, 7168, "bf16", "bf16", 0), (2003, 4096, "f32", "f32", 8),
+    # rows wider than 1024 chunks over many windows
+    (2500, 16384, "bf16", "bf16", 0), (1000, 8192, "f32", "f32", 0),
 ]
 
 
