@@ -68,6 +68,9 @@ HEADS_CASES = [
     (11, 6, 512, "f32", "f32", 512, 0, 3072),
     (4099, 7, 128, "bf16", "bf16", 128, 0, 7 * 128),                # many rows: token = row / heads
     (1500, 40, 128, "bf16", "bf16", 136, 64, 40 * 136 + 64),
+    # the widest heads (1024 bf16 / 512 fp32 values) and the narrowest, over many rows
+    (2000, 4, 1024, "bf16", "bf16", 1024, 0, 4 * 1024), (1700, 3, 512, "f32", "f32", 520, 4, 3 * 520 + 8),
+    (3001, 48, 8, "bf16", "f32", 8, 0, 48 * 8),
 ]
 
 
