@@ -166,7 +166,9 @@ def check_variant(oracle, x, res, w, dtype, fmt, tensor_scale, h, out, scale, no
 
 
 VARIANT_CASES = [(1, 128, 0), (3, 256, 16), (64, 1152, 0), (129, 2048, 128), (7, 4096, 0), (33, 7168, 0),
-                 (3, 16384, 0), (2, 32768, 0), (300, 1024, 0)]
+                 (3, 16384, 0), (2, 32768, 0), (300, 1024, 0),
+                 # long runs over many windows (ragged last window), and the widest rows
+                 (4099, 5120, 64), (1201, 32768, 0)]
 
 
 @pytest.mark.parametrize("mode", ["block", "tensor"])
