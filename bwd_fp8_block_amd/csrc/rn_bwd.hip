@@ -73,7 +73,7 @@ __device__ __forceinline__ void store_floats(float* p, const float* v, bool vec)
     }
 }
 
-template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, bool RES>
+template <int XT, int WT, int LPRC, int NV, int WGMAX, bool NT, int PD, bool ST, bool RES>
 __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
 {
     constexpr int E = Elems<XT>::value;
@@ -263,11 +263,13 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_bwd(BwdArgs a)
     };
 
     // PD row buffers in a ring: the g, x and rstd of the next PD-1 rows are in
-    // flight while the current row is reduced and written.  The streaming
-    // launch (PD = 3) runs the steady form; two buffers (few rows, rows wider
-    // than 1024 chunks) keep the guarded form, measured on MI355X the same or
-    // 0.1-0.25 us faster per call at few rows.
-    row_pipeline<PD, (PD >= 3), RowBuf>(n_it, load, process);
+    // flight while the current row is reduced and written.  ST selects the
+    // steady form.  The plain streaming launch runs three buffers in the steady
+    // form; the residual one, which loads a third row per row, runs two (one
+    // row in flight), measured faster or equal on MI355X at every shape tried; few rows
+    // and rows wider than 1024 chunks keep two buffers in the guarded form,
+    // measured the same or 0.1-0.25 us faster per call at few rows.
+    row_pipeline<PD, ST, RowBuf>(n_it, load, process);
 
     // Emit this strip's dw partial: the gpw row groups' accumulators are
     // combined in a fixed order (group 0, 1, ...) in FP64 and rounded once to
@@ -367,22 +369,30 @@ static hipError_t bwd_go(const BwdArgs& a, const Policy& p, hipStream_t s)
     // The residual form is compiled with streaming accesses only.
     const bool nt = RES || (p.flags & RN_FLAG_NT) != 0;
     if constexpr (NV <= 2) {
-        // pipeline depth is a launch choice
+        // pipeline depth and form are launch choices
         if (pd == 3) {
-            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3, RES>), g, b, 0, s, a);
-            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3, false>), g, b, 0, s, a);
+            if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 3, true, RES>), g, b, 0, s, a);
+            else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 3, true, false>), g, b, 0, s, a);
             return hipGetLastError();
         }
         if constexpr (LPRC == 64 && NV == 1) {
             if (pd == 4) {
-                if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4, RES>), g, b, 0, s, a);
-                else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4, false>), g, b, 0, s, a);
+                if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 4, true, RES>), g, b, 0, s, a);
+                else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 4, true, false>), g, b, 0, s, a);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (RES && WGMAX <= 512) {
+            // two buffers in the steady form: the residual streaming launch
+            // (groups of at most 512 lanes)
+            if (pd == 2 && (p.flags & RN_FLAG_STEADY)) {
+                hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2, true, true>), g, b, 0, s, a);
                 return hipGetLastError();
             }
         }
     }
-    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2, RES>), g, b, 0, s, a);
-    else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 2, false>), g, b, 0, s, a);
+    if (nt) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, true, 2, false, RES>), g, b, 0, s, a);
+    else if constexpr (!RES) hipLaunchKernelGGL((k_rmsnorm_bwd<XT, WT, LPRC, NV, WGMAX, false, 2, false, false>), g, b, 0, s, a);
     return hipGetLastError();
 }
 

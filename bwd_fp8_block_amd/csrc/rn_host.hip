@@ -277,19 +277,28 @@ bool bwd_one_strip(int64_t T, int64_t H, int x_dtype)
     return p.grid == 1;
 }
 
-// Backward with a residual stream: as the plain backward, except that groups
-// wider than 512 lanes keep two row buffers: the extra g_residual buffer of a
-// third does not fit the registers of a 1024-thread group (measured on MI355X:
-// bf16 T = 8192, H = 7168 with one vector per lane, 105 us with three buffers
-// against 92 us with two).  The wide-row form of the plain backward (two
-// vectors per lane, one group of at most 512 lanes, three buffers) measured
-// T = 8192 / 65536, H = 5120 63.3 / 484 us against 70.6 / 524 with one vector
-// per lane, and H = 7168 within 3% either way (T = 4096 .. 8192).
+// Backward with a residual stream: as the plain backward, except that
+//   - groups wider than 512 lanes keep two row buffers: the extra g_residual
+//     buffer of a third does not fit the registers of a 1024-thread group
+//     (measured on MI355X: bf16 T = 8192, H = 7168 with one vector per lane,
+//     105 us with three buffers against 92 us with two).  The wide-row form of
+//     the plain backward (two vectors per lane, one group of at most 512 lanes,
+//     three buffers) measured T = 8192 / 65536, H = 5120 63.3 / 484 us against
+//     70.6 / 524 with one vector per lane, and H = 7168 within 3% either way
+//     (T = 4096 .. 8192);
+//   - where the plain backward streams with three buffers, the residual one,
+//     which loads a third row for every row, streams with two in the steady
+//     form (one row of loads in flight), measured faster or equal at every
+//     shape tried on MI355X: bf16 T = 8192, H = 4096 46.3 against 47.4 us;
+//     T = 58497, H = 2048 with fp32 weight 156.6 against 162.4; T = 32768,
+//     H = 5120 231.7 against 239.5; 1-4% less over H = 256 .. 7168,
+//     T = 1024 .. 32768; T = 65536, H = 4096 375.7 against 374.6.
 int policy_bwd_residual(int64_t T, int64_t H, int x_dtype, int cu, Policy* p)
 {
     const int st = policy_bwd(T, H, x_dtype, cu, p);
     if (st != RN_OK) return st;
     if (p->wgs > 512) p->flags &= ~(7 << 4);
+    else if (((p->flags >> 4) & 7) == 3) p->flags = (p->flags & ~(7 << 4)) | (2 << 4) | rn::RN_FLAG_STEADY;
     return RN_OK;
 }
 

@@ -21,6 +21,7 @@ struct Policy {
 
 constexpr int RN_FLAG_NT = 1;    // non-temporal (streaming) loads and stores
 constexpr int RN_FLAG_ILV = 2;   // interleaved row order (see RowWalk)
+constexpr int RN_FLAG_STEADY = 8;   // with two row buffers: the steady prefetch form (see row_pipeline)
 // bits 4-6: row-buffer pipeline depth (0 = the kernel's default)
 
 // Forward forms (kernel template argument and launch_fwd's `mode`).
