@@ -77,10 +77,18 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     char* ybase = static_cast<char*>(a.y);
     char* hbase = static_cast<char*>(a.h);
 
+    // Per-head rows: the token of row r is floor(r / heads), taken as a
+    // multiply and a shift by the host's constants (division by an invariant
+    // integer, Granlund and Montgomery 1994): with l = ceil(log2 heads) and
+    // m = ceil(2^(31+l) / heads) < 2^32, floor(r * m / 2^(31+l)) equals
+    // floor(r / heads) for every r < 2^31 (rows < 2^31 is a host check).
+    auto token_of = [&](uint32_t rr) -> uint32_t {
+        return (uint32_t)(((uint64_t)rr * a.hmul) >> a.hshift);
+    };
     // Element offsets of row r in x and in y (u and h_new use plain strides).
     auto xoff = [&](int64_t r) -> int64_t {
         if constexpr (HEADS) {
-            const uint32_t rr = (uint32_t)r, t = rr / (uint32_t)a.heads;   // rows < 2^31 (host check)
+            const uint32_t rr = (uint32_t)r, t = token_of(rr);
             return (int64_t)t * a.ldx + (int64_t)(rr - t * (uint32_t)a.heads) * a.ldxh;
         } else {
             return r * a.ldx;
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(WGMAX) void k_rmsnorm_fwd(FwdArgs a)
     };
     auto yoff = [&](int64_t r) -> int64_t {
         if constexpr (HEADS) {
-            const uint32_t rr = (uint32_t)r, t = rr / (uint32_t)a.heads;
+            const uint32_t rr = (uint32_t)r, t = token_of(rr);
             return (int64_t)t * a.ldy + (int64_t)(rr - t * (uint32_t)a.heads) * a.ldyh;
         } else {
             return r * a.ldy;

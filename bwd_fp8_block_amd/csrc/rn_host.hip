@@ -830,6 +830,15 @@ int rmsnorm_fwd_heads(const void* x, int64_t ld_token, int64_t ld_head, int x_dt
     a.lpr = p.lpr;
     a.interleave = (p.flags & rn::RN_FLAG_ILV) ? 1 : 0;
     a.heads = (int)heads;
+    {
+        // floor(r / heads) = (r * m) >> (31 + l) for r < 2^31: l = ceil(log2 heads),
+        // m = ceil(2^(31+l) / heads), which is below 2^32.
+        int l = 0;
+        while ((int64_t(1) << l) < heads) ++l;
+        const uint64_t m = ((uint64_t(1) << (31 + l)) + (uint64_t)heads - 1) / (uint64_t)heads;
+        a.hmul = (uint32_t)m;
+        a.hshift = 31 + l;
+    }
     a.x = x; a.ldx = ld_token; a.ldxh = ld_head;
     a.w = w;
     a.y = y; a.ldy = ldy_token; a.ldyh = ldy_head;

@@ -33,6 +33,7 @@ struct FwdArgs {
     int lpr;                     // lanes per row group (runtime for class 64)
     int interleave;              // RN_FLAG_ILV set in the policy
     int heads;                   // per-head form: heads per token (rows = T * heads)
+    uint32_t hmul; int hshift;   // per-head form: floor(r / heads) = (r * hmul) >> hshift for r < 2^31
     const void* x; int64_t ldx;
     int64_t ldxh;                // per-head form: element stride between heads of x
     int64_t ldyh;                // per-head form: element stride between heads of y

@@ -419,3 +419,24 @@ def test_bwd_noalloc_validation(rn):
     assert call() == 8                             # no workspace argument is needed
     assert call(det=0) == 8
 
+
+
+def test_per_head_token_index_multiply_shift():
+    """The per-head forward finds the token of row r as (r * m) >> (31 + l) with
+    l = ceil(log2 heads) and m = ceil(2^(31+l) / heads) (division by an invariant
+    integer, Granlund and Montgomery 1994).  For every head count the host accepts
+    (1 .. 65535), m fits 32 bits and the quotient equals r // heads at the rows
+    where an error would show first: just below and at every multiple of heads up
+    to a bound, and the largest rows below 2^31."""
+    import numpy as np
+    top = (1 << 31) - 1
+    for d in range(1, 65536):
+        l = (d - 1).bit_length()
+        m = ((1 << (31 + l)) + d - 1) // d
+        assert m < (1 << 32)
+        q = np.arange(1, 64, dtype=np.uint64)
+        a = q * np.uint64(d)
+        n = np.concatenate([a, a - np.uint64(1), np.arange(top - 2 * d, top + 1, dtype=np.uint64)[-64:]])
+        n = n[n <= top]
+        got = (n * np.uint64(m)) >> np.uint64(31 + l)
+        assert np.array_equal(got, n // np.uint64(d)), d

@@ -71,6 +71,8 @@ HEADS_CASES = [
     # the widest heads (1024 bf16 / 512 fp32 values) and the narrowest, over many rows
     (2000, 4, 1024, "bf16", "bf16", 1024, 0, 4 * 1024), (1700, 3, 512, "f32", "f32", 520, 4, 3 * 520 + 8),
     (3001, 48, 8, "bf16", "f32", 8, 0, 48 * 8),
+    # many heads per token (the token of a row is found by a multiply and a shift)
+    (50, 1000, 8, "bf16", "bf16", 8, 0, 8000), (301, 127, 16, "bf16", "bf16", 24, 8, 127 * 24 + 8),
 ]
 
 
