@@ -1,0 +1,97 @@
+"""Seeded random shapes through the C ABI against the oracle.
+
+Row counts, row widths, dtypes and row padding are drawn at random within each
+entry point's limits (one fixed seed per op, so the cases are the same on every
+run and named by their shapes), beyond the hand-picked cases of the other parity
+tests: every launch policy the shapes select runs, with the comparison rules and
+the guard bands around every output that those tests use.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import check_dw, check_rstd, check_values
+from test_parity_gpu import check_fp8, gpu_bwd, gpu_fp8, gpu_fwd
+from workloads import Workload, generate
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+ELEMENT_BUDGET = 6_000_000        # T * H per case, so that the oracle stays fast
+
+
+def _rows(rng, H):
+    """Half the draws log-uniform over [1, tmax] (few-row launches), half uniform over
+    [tmax/4, tmax] (runs over many windows with a ragged last one)."""
+    tmax = max(1, min(20000, ELEMENT_BUDGET // H))
+    if rng.random() < 0.5:
+        return max(1, int(np.exp(rng.uniform(0.0, np.log(tmax)))))
+    return max(1, int(rng.integers(max(1, tmax // 4), tmax + 1)))
+
+
+def _row_cases(op, seed):
+    """(T, H, x dtype, w dtype, row padding in elements) for the forward or the backward."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(N_CASES):
+        xd = "f32" if rng.random() < 0.25 else "bf16"
+        wd = "f32" if xd == "f32" or rng.random() < 0.3 else "bf16"
+        e = 4 if xd == "f32" else 8                    # elements per 16-byte vector
+        hmax = {"fwd": {"bf16": 32768, "f32": 16384}, "bwd": {"bf16": 16384, "f32": 8192}}[op][xd]
+        H = max(e, int(np.exp(rng.uniform(np.log(e), np.log(hmax)))) // e * e)
+        pad = int(rng.choice([0, 0, 0, e, 2 * e, 64]))
+        cases.append((_rows(rng, H), H, xd, wd, pad))
+    return cases
+
+
+def _fp8_cases(seed):
+    """(T, H, row padding in elements) for the producer: H a multiple of 128; the padding
+    is shared by the 1-byte codes, whose row stride must stay a 16-byte multiple."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(N_CASES):
+        H = 128 * max(1, int(np.exp(rng.uniform(0.0, np.log(256)))))
+        pad = int(rng.choice([0, 0, 16, 64]))
+        cases.append((_rows(rng, H), H, pad))
+    return cases
+
+
+FWD_RANDOM = _row_cases("fwd", 71)
+BWD_RANDOM = _row_cases("bwd", 72)
+FP8_RANDOM = _fp8_cases(73)
+
+
+def _ids(cases):
+    return ["T%d-H%d-%s" % (c[0], c[1], "-".join(str(v) for v in c[2:])) for c in cases]
+
+
+@pytest.fixture(scope="module")
+def rn():
+    import bwd_fp8_block_amd as m
+    return m
+
+
+@pytest.mark.parametrize("T,H,xd,wd,pad", FWD_RANDOM, ids=_ids(FWD_RANDOM))
+def test_fwd_random_shapes(rn, oracle, T, H, xd, wd, pad):
+    d = generate(Workload("fwd", T, H, xd, wd, seed=7100 + T + H))
+    y, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6, ld_pad=pad)
+    yref, rref = oracle.rmsnorm_fwd(d["x"], d["w"], 1e-6)
+    check_rstd(rstd, rref)
+    check_values("y", y, yref, xd == "bf16")
+
+
+@pytest.mark.parametrize("k", range(N_CASES), ids=_ids(BWD_RANDOM))
+def test_bwd_random_shapes(rn, oracle, k):
+    T, H, xd, wd, pad = BWD_RANDOM[k]
+    d = generate(Workload("bwd", T, H, xd, wd, seed=7200 + T + H))
+    _, rstd = gpu_fwd(rn, d["x"], d["w"], 1e-6)
+    dx, dw = gpu_bwd(rn, d["dy"], d["x"], d["w"], rstd, k % 2 == 0, ld_pad=pad, poison=True)
+    dxref, dwref = oracle.rmsnorm_bwd(d["dy"], d["x"], d["w"], rstd.astype(np.float64))
+    check_values("dx", dx, dxref, xd == "bf16")
+    check_dw(dw, dwref)
+
+
+@pytest.mark.parametrize("T,H,pad", FP8_RANDOM, ids=_ids(FP8_RANDOM))
+def test_fp8_random_shapes(rn, oracle, T, H, pad):
+    d = generate(Workload("fp8", T, H, "bf16", "bf16", residual=True, seed=7300 + T + H))
+    h, out, scale, normed = gpu_fp8(rn, d["x"], d["residual"], d["w"], 1e-6, ld_pad=pad, scale_pad=4)
+    check_fp8(oracle, d["x"], d["residual"], d["w"], 1e-6, h, out, scale, normed)
