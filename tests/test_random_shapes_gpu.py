@@ -11,7 +11,9 @@ import pytest
 
 from gpu_common import check_dw, check_rstd, check_values
 from test_parity_gpu import check_fp8, gpu_bwd, gpu_fp8, gpu_fwd
-from workloads import Workload, generate
+from test_parity_heads_gpu import make_fused, run_heads
+from test_parity_residual_gpu import gpu_bwd_res, gpu_fwd_res
+from workloads import Workload, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +60,30 @@ def _fp8_cases(seed):
 FWD_RANDOM = _row_cases("fwd", 71)
 BWD_RANDOM = _row_cases("bwd", 72)
 FP8_RANDOM = _fp8_cases(73)
+FRES_RANDOM = _row_cases("fwd", 74)        # the residual pair has the plain ops' limits
+BRES_RANDOM = _row_cases("bwd", 75)
+
+
+def _heads_cases(seed):
+    """(T, heads, head_dim, dtype, w dtype, head stride, band offset, token stride), strides and
+    offsets in elements and 16-byte multiples; head_dim up to 128 vectors."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(N_CASES):
+        xd = "f32" if rng.random() < 0.25 else "bf16"
+        wd = "f32" if xd == "f32" or rng.random() < 0.3 else "bf16"
+        e = 4 if xd == "f32" else 8
+        D = max(e, int(np.exp(rng.uniform(np.log(e), np.log(128 * e)))) // e * e)
+        nh = max(1, int(np.exp(rng.uniform(0.0, np.log(1000 if rng.random() < 0.15 else 64)))))
+        ldh = D + e * int(rng.choice([0, 0, 1, 2]))
+        off = e * int(rng.choice([0, 0, 1, 8]))
+        ldt = off + (nh - 1) * ldh + D + e * int(rng.choice([0, 0, 1, 4]))
+        T = _rows(rng, nh * D)
+        cases.append((T, nh, D, xd, wd, ldh, off, ldt))
+    return cases
+
+
+HEADS_RANDOM = _heads_cases(76)
 
 
 def _ids(cases):
@@ -95,3 +121,36 @@ def test_fp8_random_shapes(rn, oracle, T, H, pad):
     d = generate(Workload("fp8", T, H, "bf16", "bf16", residual=True, seed=7300 + T + H))
     h, out, scale, normed = gpu_fp8(rn, d["x"], d["residual"], d["w"], 1e-6, ld_pad=pad, scale_pad=4)
     check_fp8(oracle, d["x"], d["residual"], d["w"], 1e-6, h, out, scale, normed)
+
+
+@pytest.mark.parametrize("T,H,xd,wd,pad", FRES_RANDOM, ids=_ids(FRES_RANDOM))
+def test_fwd_residual_random_shapes(rn, oracle, T, H, xd, wd, pad):
+    d = generate(Workload("fres", T, H, xd, wd, residual=True, seed=7400 + T + H))
+    y, h, rstd = gpu_fwd_res(rn, d["x"], d["residual"], d["w"], 1e-6, ld_pad=pad)
+    yref, rref, href = oracle.rmsnorm_fwd_residual(d["x"], d["residual"], d["w"], 1e-6)
+    assert np.array_equal(h, href), "h_new not bit-exact"
+    check_rstd(rstd, rref)
+    check_values("y", y, yref, xd == "bf16")
+
+
+@pytest.mark.parametrize("T,H,xd,wd,pad", BRES_RANDOM, ids=_ids(BRES_RANDOM))
+def test_bwd_residual_random_shapes(rn, oracle, T, H, xd, wd, pad):
+    d = generate(Workload("bres", T, H, xd, wd, residual=True, g_residual=True, seed=7500 + T + H))
+    _, h, rstd = gpu_fwd_res(rn, d["x"], d["residual"], d["w"], 1e-6)
+    dx, dw = gpu_bwd_res(rn, d["dy"], h, d["w"], rstd, d["g_residual"], ld_pad=pad, poison=True)
+    dxref, dwref = oracle.rmsnorm_bwd_residual(d["dy"], h, d["w"], rstd.astype(np.float64), d["g_residual"])
+    check_values("dx_total", dx, dxref, xd == "bf16")
+    check_dw(dw, dwref)
+
+
+@pytest.mark.parametrize("T,nh,D,xd,wd,ldh,off,ldt", HEADS_RANDOM, ids=_ids(HEADS_RANDOM))
+def test_heads_random_shapes(rn, oracle, T, nh, D, xd, wd, ldh, off, ldt):
+    host = make_fused(T, ldt, xd, 7600 + T + nh + D)
+    rng = np.random.default_rng(7700 + D)
+    w = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    w = to_bf16_bits(w) if wd == "bf16" else w
+    y, rstd, after = run_heads(rn, host, nh, D, ldh, off, w, 1e-6)
+    assert np.array_equal(after, host), "input modified"
+    yref, rref = oracle.rmsnorm_fwd_heads(np.ascontiguousarray(host[:, off:]), nh, D, w, 1e-6, ld_head=ldh)
+    check_rstd(rstd.reshape(-1), rref.reshape(-1))
+    check_values("y", y.reshape(T * nh, D), yref.reshape(T * nh, D), xd == "bf16")
