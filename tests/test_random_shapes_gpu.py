@@ -13,6 +13,7 @@ from gpu_common import check_dw, check_rstd, check_values
 from test_parity_gpu import check_fp8, gpu_bwd, gpu_fp8, gpu_fwd
 from test_parity_heads_gpu import make_fused, run_heads
 from test_parity_residual_gpu import gpu_bwd_res, gpu_fwd_res
+from test_parity_variants_gpu import _lp, check_variant, run_variant
 from workloads import Workload, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -86,6 +87,24 @@ def _heads_cases(seed):
 HEADS_RANDOM = _heads_cases(76)
 
 
+def _variant_cases(seed):
+    """(T, H, row padding, row dtype, code format, per-tensor scale or None, normed written)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for (T, H, pad) in _fp8_cases(seed):
+        dtype = str(rng.choice(["bf16", "f16"]))
+        fmt = str(rng.choice(["e4m3", "e5m2"]))
+        ts = None
+        if rng.random() < 0.5:        # a given per-tensor scale, log-uniform around the codes' range
+            top = 448.0 if fmt == "e4m3" else 57344.0
+            ts = float(np.float32(np.exp2(rng.uniform(-4.0, 4.0)) * 4.0 / top))
+        cases.append((T, H, pad, dtype, fmt, ts, bool(rng.random() < 0.7)))
+    return cases
+
+
+VARIANT_RANDOM = _variant_cases(77)
+
+
 def _ids(cases):
     return ["T%d-H%d-%s" % (c[0], c[1], "-".join(str(v) for v in c[2:])) for c in cases]
 
@@ -154,3 +173,19 @@ def test_heads_random_shapes(rn, oracle, T, nh, D, xd, wd, ldh, off, ldt):
     yref, rref = oracle.rmsnorm_fwd_heads(np.ascontiguousarray(host[:, off:]), nh, D, w, 1e-6, ld_head=ldh)
     check_rstd(rstd.reshape(-1), rref.reshape(-1))
     check_values("y", y.reshape(T * nh, D), yref.reshape(T * nh, D), xd == "bf16")
+
+
+@pytest.mark.parametrize("T,H,pad,dtype,fmt,ts,with_normed", VARIANT_RANDOM, ids=_ids(VARIANT_RANDOM))
+def test_variant_random_shapes(rn, oracle, T, H, pad, dtype, fmt, ts, with_normed):
+    rng = np.random.default_rng(7800 + T + H)
+    x = _lp(rng.standard_normal((T, H)), dtype)
+    res = _lp(rng.standard_normal((T, H)), dtype)
+    w = _lp(1 + 0.1 * rng.standard_normal(H), dtype)
+    h, out, scale, normed = run_variant(rn, x, res, w, dtype, fmt, ts, ld_pad=pad)
+    check_variant(oracle, x, res, w, dtype, fmt, ts, h, out, scale, normed)
+    if not with_normed:
+        # without normed_out the codes and scales are those of the call that writes it
+        h2, out2, scale2, n2 = run_variant(rn, x, res, w, dtype, fmt, ts, with_normed=False, ld_pad=pad)
+        assert n2 is None and np.array_equal(h2, h) and np.array_equal(out2, out)
+        if scale is not None:
+            assert np.array_equal(scale2[:, :T].view(np.uint32), scale[:, :T].view(np.uint32))
