@@ -14,6 +14,7 @@ import torch
 
 from gpu_common import (as_f64, assert_guards, check_dw, check_rstd, check_values, compare_all_rows, edge_inputs,
                         guarded_matrix, strided_dev, to_dev, to_host, torch_dtype)
+from gpu_ops import check_fp8, gpu_bwd, gpu_fp8, gpu_fwd
 from workloads import to_bf16_bits
 from workloads import CONFIGS, Workload, generate
 
@@ -26,38 +27,6 @@ def rn():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     return m
 
-
-def gpu_fwd(rn, x: np.ndarray, w: np.ndarray, eps: float, ld_pad=0):
-    T, H = x.shape
-    xd, wd = to_dev(x), to_dev(w)
-    ld = H + ld_pad
-    yfull, y = guarded_matrix(T, H, torch_dtype(x), ld)
-    rfull, rstd = guarded_matrix(1, T, torch.float32)
-    rstd = rstd.view(T)
-    rn.rmsnorm_fwd(xd, wd, y, rstd, eps)
-    torch.cuda.synchronize()
-    assert_guards(yfull, T, H, ld, name="y")
-    assert_guards(rfull, 1, T, T, name="rstd")
-    return to_host(y) if T else np.zeros((0, H), x.dtype), to_host(rstd)
-
-
-def gpu_bwd(rn, dy, x, w, rstd, det, ld_pad=0, poison=False):
-    T, H = x.shape
-    dyd, xd, wd = to_dev(dy), to_dev(x), to_dev(w)
-    rd = torch.from_numpy(np.ascontiguousarray(rstd, dtype=np.float32)).cuda()
-    ld = H + ld_pad
-    dxfull, dx = guarded_matrix(T, H, torch_dtype(x), ld)
-    dwfull, dw = guarded_matrix(1, H, torch.float32)
-    dw = dw.view(H)
-    nbytes = rn.rmsnorm_bwd_workspace_bytes(T, H)
-    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device="cuda")
-    if poison:
-        ws.fill_(float("nan"))
-    rn.rmsnorm_bwd(dyd, xd, wd, rd, dx, dw, deterministic=det, workspace=ws)
-    torch.cuda.synchronize()
-    assert_guards(dxfull, T, H, ld, name="dx")
-    assert_guards(dwfull, 1, H, H, name="dw")
-    return to_host(dx) if T else np.zeros((0, H), x.dtype), to_host(dw)
 
 
 # ----------------------------------------------------------------------------
@@ -341,45 +310,6 @@ def test_bwd_one_strip_needs_no_workspace(rn, oracle, T, H, xd, det):
 # ----------------------------------------------------------------------------
 # fused residual add + RMSNorm + fp8 block quant
 # ----------------------------------------------------------------------------
-def gpu_fp8(rn, x, res, w, eps, ld_pad=0, scale_pad=0):
-    T, H = x.shape
-    ld = H + ld_pad
-    xd, wd = to_dev(x), to_dev(w)
-    rfull, r = guarded_matrix(T, H, torch.bfloat16, ld)
-    if T:
-        r.copy_(to_dev(res))
-    ofull, o = guarded_matrix(T, H, torch.uint8, ld)
-    nfull, n = guarded_matrix(T, H, torch.bfloat16, ld)
-    sld = (T + 3) // 4 * 4 + scale_pad
-    sfull, s = guarded_matrix(H // 128, sld, torch.float32)
-    rn.add_rmsnorm_fp8_block_quant(xd, r, wd, o, s, n, eps)
-    torch.cuda.synchronize()
-    assert_guards(rfull, T, H, ld, name="residual")
-    assert_guards(ofull, T, H, ld, name="out")
-    assert_guards(nfull, T, H, ld, name="normed")
-    sh = to_host(s)
-    assert np.all(np.isnan(sh[:, T:])), "scale padding rows were written"
-    assert_guards(sfull, H // 128, sld, sld, name="block_scale")
-    return to_host(r), to_host(o), sh, to_host(n)
-
-
-def check_fp8(oracle, x, res, w, eps, h, out, scale, normed):
-    T = x.shape[0]
-    ref = oracle.add_rmsnorm_fp8(x, res, w, eps)
-    assert np.array_equal(h, ref["h"]), "residual not bit-exact"
-    check_values("normed", normed, ref["normed"], True)
-    sref, cref = oracle.block_quant_e4m3(normed, scale_ld=scale.shape[1])
-    assert np.array_equal(scale[:, :T].view(np.uint32), sref[:, :T].view(np.uint32)), "block scales not bit-exact"
-    bad = np.argwhere(out != cref)
-    assert bad.size == 0, "fp8 codes differ at %s (gpu 0x%02x, oracle 0x%02x)" % (
-        bad[0], out[tuple(bad[0])], cref[tuple(bad[0])])
-    # the oracle's own end-to-end codes: equal wherever its bf16 normed equals the GPU's
-    same = ref["normed_bf16"] == normed
-    assert np.array_equal(ref["codes"][same & np.repeat(
-        (ref["scale"][:, :T].T == scale[:, :T].T), 128, axis=1)], out[same & np.repeat(
-            (ref["scale"][:, :T].T == scale[:, :T].T), 128, axis=1)])
-    return float(same.mean())
-
 
 FP8_CASES = [(1, 128, 0), (3, 256, 16), (5, 384, 0), (64, 1152, 0), (129, 2048, 128), (7, 4096, 0),
              (33, 7168, 0), (6, 8192, 0), (3, 16384, 0), (2, 32768, 0), (300, 1024, 0),

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import (as_f64, assert_guards, check_rstd, check_values, compare_all_rows, guarded_matrix, to_dev,
-                        to_host)
+from gpu_common import as_f64, check_rstd, check_values, compare_all_rows, to_dev, to_host
+from gpu_ops import heads_view, make_fused, run_heads
 from workloads import CONFIGS, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -20,38 +20,6 @@ def rn():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     return m
 
-
-def make_fused(T, ld_t, dt, seed):
-    rng = np.random.default_rng(seed)
-    a = rng.standard_normal((T, ld_t)).astype(np.float32)
-    return to_bf16_bits(a) if dt == "bf16" else a
-
-
-def heads_view(dev_full, T, nh, D, ld_t, ld_h, off):
-    return torch.as_strided(dev_full, (T, nh, D), (ld_t, ld_h, 1), storage_offset=off)
-
-
-def run_heads(rn, host_full, nh, D, ld_h, off, w, eps, with_rstd=True, in_place=False):
-    T, ld_t = host_full.shape
-    dt = torch.bfloat16 if host_full.dtype == np.uint16 else torch.float32
-    full = to_dev(host_full)
-    x = heads_view(full, T, nh, D, ld_t, ld_h, off)
-    if in_place:
-        y, yfull = x, None
-    else:
-        yfull, y2 = guarded_matrix(T, nh * D, dt)
-        y = y2.view(T, nh, D) if T else y2.view(0, nh, D)
-    rfull, rstd = guarded_matrix(1, T * nh, torch.float32)
-    rstd = rstd.view(T * nh)
-    rn.rmsnorm_fwd_heads(x, to_dev(w), y, rstd if with_rstd else None, eps)
-    torch.cuda.synchronize()
-    if yfull is not None:
-        assert_guards(yfull, T, nh * D, nh * D, name="y")
-    assert_guards(rfull, 1, T * nh, T * nh, name="rstd")
-    r = to_host(rstd).reshape(T, nh)
-    if not with_rstd:
-        assert np.all(np.isnan(r)), "rstd written although not requested"
-    return to_host(y.contiguous()), r, to_host(full)
 
 
 HEADS_CASES = [

@@ -12,6 +12,7 @@ import torch
 
 from gpu_common import (as_f64, assert_guards, check_dw, check_rstd, check_values, compare_all_rows, edge_inputs,
                         guarded_matrix, strided_dev, to_dev, to_host, torch_dtype)
+from gpu_ops import gpu_bwd_res, gpu_fwd_res
 from workloads import CONFIGS, Workload, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -23,63 +24,6 @@ def rn():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     return m
 
-
-def gpu_fwd_res(rn, x, u, w, eps, ld_pad=0, inplace=None):
-    """Runs rmsnorm_fwd_residual; inplace in (None, "x", "u") writes h_new over that input."""
-    T, H = x.shape
-    ld = H + ld_pad
-    dt = torch_dtype(x)
-    xfull, xd = guarded_matrix(T, H, dt, ld)
-    ufull, ud = guarded_matrix(T, H, dt, ld)
-    if T:
-        xd.copy_(to_dev(x))
-        ud.copy_(to_dev(u))
-    yfull, y = guarded_matrix(T, H, dt, ld)
-    if inplace == "x":
-        hfull, h = xfull, xd
-    elif inplace == "u":
-        hfull, h = ufull, ud
-    else:
-        hfull, h = guarded_matrix(T, H, dt, ld)
-    rfull, rstd = guarded_matrix(1, T, torch.float32)
-    rstd = rstd.view(T)
-    rn.rmsnorm_fwd_residual(xd, ud, to_dev(w), y, h, rstd, eps)
-    torch.cuda.synchronize()
-    for f, n in ((xfull, "x"), (ufull, "u"), (yfull, "y"), (hfull, "h_out")):
-        assert_guards(f, T, H, ld, name=n)
-    assert_guards(rfull, 1, T, T, name="rstd")
-    empty = np.zeros((0, H), x.dtype)
-    return (to_host(y) if T else empty), (to_host(h) if T else empty), to_host(rstd)
-
-
-def gpu_bwd_res(rn, dy, h, w, rstd, gres, ld_pad=0, inplace=False, poison=False):
-    T, H = h.shape
-    ld = H + ld_pad
-    dt = torch_dtype(h)
-    rd = torch.from_numpy(np.ascontiguousarray(rstd, dtype=np.float32)).cuda()
-    dxfull, dx = guarded_matrix(T, H, dt, ld)
-    if inplace:
-        if T:
-            dx.copy_(to_dev(gres))
-        g, gfull = dx, None
-    else:
-        gfull, g = guarded_matrix(T, H, dt, ld)
-        if T:
-            g.copy_(to_dev(gres))
-    dwfull, dw = guarded_matrix(1, H, torch.float32)
-    dw = dw.view(H)
-    ws = torch.empty(max(rn.rmsnorm_bwd_workspace_bytes(T, H) // 4, 1), dtype=torch.float32, device="cuda")
-    if poison:
-        ws.fill_(float("nan"))
-    rn.rmsnorm_bwd_residual(to_dev(dy), to_dev(h), to_dev(w), rd, g, dx, dw, deterministic=True, workspace=ws)
-    torch.cuda.synchronize()
-    assert_guards(dxfull, T, H, ld, name="dx")
-    if gfull is not None:
-        assert_guards(gfull, T, H, ld, name="g_residual")
-        if T:
-            assert np.array_equal(to_host(g), gres), "g_residual was modified"
-    assert_guards(dwfull, 1, H, H, name="dw")
-    return (to_host(dx) if T else np.zeros((0, H), h.dtype)), to_host(dw)
 
 
 RES_FWD_CASES = [

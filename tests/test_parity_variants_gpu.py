@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import assert_guards, check_values, guarded_matrix, to_host
+from gpu_common import to_host
+from gpu_ops import check_variant, dec16, dev16, host16, lp16, run_variant
 from workloads import CONFIGS, Workload, generate
 
 pytestmark = pytest.mark.gpu
@@ -80,90 +81,6 @@ def test_cvt_e5m2_matches_oracle_encoder(rn, oracle):
 # ----------------------------------------------------------------------------
 # the producer variants
 # ----------------------------------------------------------------------------
-def _lp(a, dtype):
-    a = np.asarray(a, np.float32)
-    if dtype == "bf16":
-        from workloads import to_bf16_bits
-        return to_bf16_bits(a)
-    return a.astype(np.float16).view(np.uint16)
-
-
-def _dev16(bits, dtype):
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
-    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
-
-
-def _host16(t):
-    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
-
-
-def _dec16(b, dtype):
-    if dtype == "bf16":
-        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return b.view(np.float16).astype(np.float64)
-
-
-def check_normed(normed, ref, dtype):
-    if dtype == "bf16":
-        return check_values("normed", normed, ref, True)
-    g = _dec16(normed, "f16")
-    err = np.abs(g - ref)
-    assert err.max() <= 5e-2
-    spacing = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -14))) - 10)
-    bad = err > spacing + 2.0 ** -20 * np.max(np.abs(ref), axis=-1, keepdims=True)
-    assert not bad.any(), "normed: %d values beyond one fp16 spacing" % int(bad.sum())
-
-
-def run_variant(rn, x, res, w, dtype, fmt, tensor_scale=None, with_normed=True, ld_pad=0, scale_pad=4, eps=1e-6):
-    T, H = x.shape
-    ld = H + ld_pad
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
-    xd, wd = _dev16(x, dtype), _dev16(w, dtype)
-    rfull, r = guarded_matrix(T, H, torch.bfloat16, ld)
-    rfull, r = rfull.view(tdt), r.view(tdt)
-    if T:
-        r.copy_(_dev16(res, dtype))
-    ofull, o = guarded_matrix(T, H, torch.uint8, ld)
-    nfull = n = None
-    if with_normed:
-        nfull, n = guarded_matrix(T, H, torch.bfloat16, ld)
-        nfull, n = nfull.view(tdt), n.view(tdt)
-    sfull = s = ts = None
-    if tensor_scale is None:
-        sld = (T + 3) // 4 * 4 + scale_pad
-        sfull, s = guarded_matrix(H // 128, sld, torch.float32)
-    else:
-        ts = torch.tensor([tensor_scale], dtype=torch.float32, device="cuda")
-    rn.add_rmsnorm_fp8_quant(xd, r, wd, o, eps, out_format=fmt, block_scale=s, tensor_scale=ts, normed_out=n)
-    torch.cuda.synchronize()
-    assert_guards(rfull.view(torch.bfloat16), T, H, ld, name="residual")
-    assert_guards(ofull, T, H, ld, name="out")
-    if nfull is not None:
-        assert_guards(nfull.view(torch.bfloat16), T, H, ld, name="normed")
-    sh = None
-    if sfull is not None:
-        sh = to_host(s)
-        assert np.all(np.isnan(sh[:, T:])), "scale padding rows were written"
-        assert_guards(sfull, H // 128, s.shape[1], s.shape[1], name="block_scale")
-    return _host16(r), to_host(o), sh, (_host16(n) if n is not None else None)
-
-
-def check_variant(oracle, x, res, w, dtype, fmt, tensor_scale, h, out, scale, normed, eps=1e-6):
-    T = x.shape[0]
-    ref = oracle.add_rmsnorm_quant(x, res, w, eps, dtype, fmt, tensor_scale or 0.0)
-    assert np.array_equal(h, ref["h"]), "residual not bit-exact"
-    if normed is None:
-        normed = ref["normed_lp"]                     # codes then checked where the oracle's normed is exact
-    else:
-        check_normed(normed, ref["normed"], dtype)
-    sref, cref = oracle.quant_lp(normed, dtype, fmt, tensor_scale or 0.0,
-                                 scale_ld=scale.shape[1] if scale is not None else None)
-    if scale is not None:
-        assert np.array_equal(scale[:, :T].view(np.uint32), sref[:, :T].view(np.uint32)), "block scales differ"
-    bad = np.argwhere(out != cref)
-    assert bad.size == 0, "codes differ at %s (gpu 0x%02x, oracle 0x%02x)" % (
-        bad[0], out[tuple(bad[0])], cref[tuple(bad[0])])
-
 
 VARIANT_CASES = [(1, 128, 0), (3, 256, 16), (64, 1152, 0), (129, 2048, 128), (7, 4096, 0), (33, 7168, 0),
                  (3, 16384, 0), (2, 32768, 0), (300, 1024, 0),
@@ -176,9 +93,9 @@ VARIANT_CASES = [(1, 128, 0), (3, 256, 16), (64, 1152, 0), (129, 2048, 128), (7,
 @pytest.mark.parametrize("T,H,pad", VARIANT_CASES)
 def test_variant_parity(rn, oracle, T, H, pad, dtype, fmt, mode):
     rng = np.random.default_rng(9000 + T + H)
-    x = _lp(rng.standard_normal((T, H)), dtype)
-    res = _lp(rng.standard_normal((T, H)), dtype)
-    w = _lp(1 + 0.1 * rng.standard_normal(H), dtype)
+    x = lp16(rng.standard_normal((T, H)), dtype)
+    res = lp16(rng.standard_normal((T, H)), dtype)
+    w = lp16(1 + 0.1 * rng.standard_normal(H), dtype)
     ts = None if mode == "block" else float(np.float32(0.01 if fmt == "e4m3" else 2.0 ** -12))
     h, out, scale, normed = run_variant(rn, x, res, w, dtype, fmt, ts, ld_pad=pad)
     check_variant(oracle, x, res, w, dtype, fmt, ts, h, out, scale, normed)
@@ -190,10 +107,10 @@ def test_tensor_scale_saturation_and_signs(rn, oracle, fmt):
     enough that most round to (signed) zero, and a row that cancels to zero."""
     T, H = 6, 512
     rng = np.random.default_rng(82)
-    x = _lp(rng.standard_normal((T, H)), "bf16")
-    res = _lp(rng.standard_normal((T, H)), "bf16")
+    x = lp16(rng.standard_normal((T, H)), "bf16")
+    res = lp16(rng.standard_normal((T, H)), "bf16")
     res[0] = x[0] ^ 0x8000
-    w = _lp(1 + 0.1 * rng.standard_normal(H), "bf16")
+    w = lp16(1 + 0.1 * rng.standard_normal(H), "bf16")
     for ts in (1e-6, 1e3, 2.0 ** -100, 3.0e38):
         h, out, _, normed = run_variant(rn, x, res, w, "bf16", fmt, float(np.float32(ts)))
         check_variant(oracle, x, res, w, "bf16", fmt, float(np.float32(ts)), h, out, None, normed)
@@ -202,9 +119,9 @@ def test_tensor_scale_saturation_and_signs(rn, oracle, fmt):
 def test_variant_without_normed_matches(rn, oracle):
     T, H = 17, 2048
     rng = np.random.default_rng(83)
-    x = _lp(rng.standard_normal((T, H)), "f16")
-    res = _lp(rng.standard_normal((T, H)), "f16")
-    w = _lp(1 + 0.1 * rng.standard_normal(H), "f16")
+    x = lp16(rng.standard_normal((T, H)), "f16")
+    res = lp16(rng.standard_normal((T, H)), "f16")
+    w = lp16(1 + 0.1 * rng.standard_normal(H), "f16")
     for ts in (None, 0.004):
         _, o1, s1, n1 = run_variant(rn, x, res, w, "f16", "e5m2", ts)
         _, o2, s2, n2 = run_variant(rn, x, res, w, "f16", "e5m2", ts, with_normed=False)
@@ -219,15 +136,15 @@ def test_variant_base_form_is_the_block_quant_entry(rn):
     T, H = 40, 1024
     d = generate(Workload("v", T, H, "bf16", "bf16", residual=True, seed=84))
     h1, o1, s1, n1 = run_variant(rn, d["x"], d["residual"], d["w"], "bf16", "e4m3")
-    xd, wd = _dev16(d["x"], "bf16"), _dev16(d["w"], "bf16")
-    r = _dev16(d["residual"], "bf16").clone()
+    xd, wd = dev16(d["x"], "bf16"), dev16(d["w"], "bf16")
+    r = dev16(d["residual"], "bf16").clone()
     o = torch.empty(T, H, dtype=torch.uint8, device="cuda")
     s = torch.full((H // 128, (T + 3) // 4 * 4 + 4), float("nan"), device="cuda")
     n = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     rn.add_rmsnorm_fp8_block_quant(xd, r, wd, o, s, n, 1e-6)
     torch.cuda.synchronize()
-    assert np.array_equal(_host16(r), h1) and np.array_equal(to_host(o), o1)
-    assert np.array_equal(_host16(n), n1) and np.array_equal(to_host(s)[:, :T], s1[:, :T])
+    assert np.array_equal(host16(r), h1) and np.array_equal(to_host(o), o1)
+    assert np.array_equal(host16(n), n1) and np.array_equal(to_host(s)[:, :T], s1[:, :T])
 
 
 def test_variant_validation(rn):
@@ -258,7 +175,7 @@ def test_config_variants(rn, oracle, name, dtype, fmt, ts):
     wl = CONFIGS[name]
     d = generate(wl)
     if dtype == "f16":            # the same draws, rounded to fp16 instead of bf16
-        conv = lambda b: _lp(_dec16(b, "bf16"), "f16")
+        conv = lambda b: lp16(dec16(b, "bf16"), "f16")
         x, res, w = conv(d["x"]), conv(d["residual"]), conv(d["w"])
     else:
         x, res, w = d["x"], d["residual"], d["w"]

@@ -10,10 +10,8 @@ import numpy as np
 import pytest
 
 from gpu_common import check_dw, check_rstd, check_values
-from test_parity_gpu import check_fp8, gpu_bwd, gpu_fp8, gpu_fwd
-from test_parity_heads_gpu import make_fused, run_heads
-from test_parity_residual_gpu import gpu_bwd_res, gpu_fwd_res
-from test_parity_variants_gpu import _lp, check_variant, run_variant
+from gpu_ops import (check_fp8, check_variant, gpu_bwd, gpu_bwd_res, gpu_fp8, gpu_fwd, gpu_fwd_res, lp16,
+                     make_fused, run_heads, run_variant)
 from workloads import Workload, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -178,9 +176,9 @@ def test_heads_random_shapes(rn, oracle, T, nh, D, xd, wd, ldh, off, ldt):
 @pytest.mark.parametrize("T,H,pad,dtype,fmt,ts,with_normed", VARIANT_RANDOM, ids=_ids(VARIANT_RANDOM))
 def test_variant_random_shapes(rn, oracle, T, H, pad, dtype, fmt, ts, with_normed):
     rng = np.random.default_rng(7800 + T + H)
-    x = _lp(rng.standard_normal((T, H)), dtype)
-    res = _lp(rng.standard_normal((T, H)), dtype)
-    w = _lp(1 + 0.1 * rng.standard_normal(H), dtype)
+    x = lp16(rng.standard_normal((T, H)), dtype)
+    res = lp16(rng.standard_normal((T, H)), dtype)
+    w = lp16(1 + 0.1 * rng.standard_normal(H), dtype)
     h, out, scale, normed = run_variant(rn, x, res, w, dtype, fmt, ts, ld_pad=pad)
     check_variant(oracle, x, res, w, dtype, fmt, ts, h, out, scale, normed)
     if not with_normed:
