@@ -57,7 +57,27 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    build_demo()
     return LIB
+
+
+DEMO_SRC = os.path.join(HERE, "examples", "c_abi_demo.c")
+DEMO = os.path.join(HERE, "c_abi_demo")
+
+
+def build_demo() -> str:
+    """The plain-C example program (host code only): gcc against the HIP runtime's C
+    API and the library just built, found next to the program at run time."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the example program")
+    tmp = DEMO + ".tmp%d" % os.getpid()
+    _run([cc, "-O2", "-std=c99", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(rocm, "include"),
+          DEMO_SRC, "-o", tmp, "-L" + HERE, "-lrmsnorm_gfx950", "-L" + os.path.join(rocm, "lib"), "-lamdhip64",
+          "-lm", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")])
+    os.replace(tmp, DEMO)
+    return DEMO
 
 
 if __name__ == "__main__":
